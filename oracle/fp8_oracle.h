@@ -1,0 +1,88 @@
+/*
+ * fp8_oracle.h -- plain, slow, single-threaded CPU oracle for the FP8
+ * scaled-cast path (quantize: amax -> scale -> cast; dequantize).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+ * CPU-baseline leg of the benchmark may load this library.  It shares no
+ * code, header, table or constant with the HIP library in
+ * dequantize_amax_reduce_amd/csrc and must never be used as a fallback for it.
+ *
+ * Sources (the pages this follows):
+ *  - ColossalAI `colossalai/quantization/fp8.py` (v0.4.4 mirror page),
+ *    functions cast_to_fp8 and cast_from_fp8: per-tensor and per-channel
+ *    scaled casts and their inverse.
+ *  - "5 Utils" (DeepEP utils notes), section on per_token_cast_to_fp8:
+ *    the per-128-element-group quantize.
+ *  - "FP8 (8 bits) & FP16 (16 bits)" (CSDN notes on fp8_cast_bf16), sections
+ *    weight_dequant and weight_dequant_kernel: the 128x128 block dequant.
+ *
+ * All floating-point arithmetic is IEEE binary32 (the pages call .float()
+ * before every reduction and product), evaluated on x86-64 SSE with no FMA
+ * contraction and no flush-to-zero.  Every function checks MXCSR first.
+ *
+ * Parity pins: every function here is pinned by the CPU tests in tests/
+ * (closed forms, exhaustive codes, structured brute force against an
+ * exact-rational nearest-value search, invariants, metamorphic scaling).
+ * The only "parity unpinned" item is the exact NaN code emitted for NaN
+ * input (NaN outputs are compared by class).
+ */
+#ifndef FP8_ORACLE_H
+#define FP8_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types (oracle-local numbering) */
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_F16 = 2 };
+/* fp8 formats (oracle-local numbering) */
+enum { ORC_E4M3FN = 0, ORC_E5M2 = 1 };
+
+/* Returns 0 when the FPU state is IEEE (no FTZ/DAZ), nonzero otherwise. */
+int oracle_fpu_check(void);
+
+/* --- element codecs ---------------------------------------------------- */
+float    oracle_fp8_decode(uint8_t code, int fmt);
+uint8_t  oracle_fp8_encode(float v, int fmt);
+float    oracle_fp8_max(int fmt);
+uint16_t oracle_bf16_from_f32(float v);
+float    oracle_f32_from_bf16(uint16_t b);
+uint16_t oracle_f16_from_f32(float v);
+float    oracle_f32_from_f16(uint16_t h);
+
+/* array forms, for tests */
+void oracle_fp8_encode_array(const float* v, int64_t n, int fmt, uint8_t* out);
+void oracle_fp8_decode_array(const uint8_t* c, int64_t n, int fmt, float* out);
+void oracle_bf16_from_f32_array(const float* v, int64_t n, uint16_t* out);
+void oracle_f16_from_f32_array(const float* v, int64_t n, uint16_t* out);
+
+/* --- steps ------------------------------------------------------------- */
+/* max |x_i| over n elements, as binary32; NaN anywhere gives NaN; n=0 gives 0 */
+float oracle_amax(const void* x, int dtype, int64_t n);
+/* per-tensor guard + scale: a = amax>0 ? amax : 1; scale = fp8_max/a; scale_inv = 1/scale */
+void  oracle_per_tensor_scale(float amax, int fmt, float* scale, float* scale_inv);
+/* q_i = enc(fl32(fp32(x_i) * scale)) for i in [0, n) */
+void  oracle_scale_and_cast(const void* x, int dtype, int64_t n, float scale, int fmt, uint8_t* q);
+
+/* --- whole operations -------------------------------------------------- */
+int oracle_cast_per_tensor(const void* x, int dtype, int64_t n, int fmt,
+                           uint8_t* q, float* scale_inv /*[1]*/);
+int oracle_cast_per_channel(const void* x, int dtype, int64_t rows, int64_t cols, int fmt,
+                            uint8_t* q, float* scale_inv /*[rows]*/);
+int oracle_cast_per_group128(const void* x, int dtype, int64_t rows, int64_t cols, int fmt,
+                             uint8_t* q, float* scale_inv /*[rows][cols/128]*/);
+int oracle_dequant_per_tensor(const uint8_t* q, int fmt, int64_t n, const float* scale_inv,
+                              void* y, int ydtype);
+int oracle_dequant_per_channel(const uint8_t* q, int fmt, int64_t rows, int64_t cols,
+                               const float* scale_inv, void* y, int ydtype);
+int oracle_dequant_per_group128(const uint8_t* q, int fmt, int64_t rows, int64_t cols,
+                                const float* scale_inv, void* y, int ydtype);
+int oracle_weight_dequant_block128(const uint8_t* q, int fmt, int64_t M, int64_t N,
+                                   const float* scale_inv, void* y, int ydtype);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
