@@ -1,0 +1,323 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP8 scaled-cast hot path on one MI355X.
+
+One step = the per-128-group quantize/dequant round trip on the LLM
+activation workload: bf16 x [16384, 7168] (N(0,1), 0.1 % of channels x50)
+-> fp8q_cast_per_group128 -> e4m3fn q + float32 scale_inv [16384, 56]
+-> fp8q_dequant_per_group128 -> bf16 [16384, 7168].  Inputs are resident in
+HBM before the timed region; three buffer sets rotate so that a step does not
+re-read what the previous one left in the 256 MB Infinity Cache.
+
+`value` = algorithmic bytes of the step (every byte the method must read and
+write, scales included) / wall time per step, in GB/s.  HIP events recorded on
+the launch stream around each kernel give the per-kernel average duration
+used for the roofline of the dominant kernel (the group cast).  The other
+hot-path operations (block dequant, per-tensor, per-channel, amax) are timed
+on their own workloads after the main loop, with a cache flush between
+iterations outside the events, and reported under "rows".
+
+The CPU oracle is timed on the host over the same activation workload
+(single-threaded, as written) as a reported baseline.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-rows] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E peak, 8 TB/s
+METRIC = "quantize/dequant GB/s and % of HBM peak, per-128-group bf16→e4m3"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-rows", action="store_true", help="skip the per-row breakdown")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
+    ap.add_argument("--rows-iters", type=int, default=10)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the row/group/block kernels shard by rows with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import dequantize_amax_reduce_amd as fq
+    from dequantize_amax_reduce_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    st = torch.cuda.Stream(device=dev)
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    # ------------------------------------------------------------------ inputs
+    R, C = 16384, 7168
+    G = C // 128
+    log(f"generating activation workload bf16 [{R}, {C}]")
+    xh, _ = W.activation_outlier_channels(rows=R, cols=C, seed=3)
+    x0 = torch.from_numpy(xh).view(torch.int16).view(torch.bfloat16).to(dev)
+    NSETS = 3
+    sets = []
+    for i in range(NSETS):
+        sets.append(dict(
+            x=x0 if i == 0 else x0.clone(),
+            q=torch.empty((R, C), dtype=torch.uint8, device=dev),
+            s=torch.empty((R, G), dtype=torch.float32, device=dev),
+            y=torch.empty((R, C), dtype=torch.bfloat16, device=dev),
+        ))
+    torch.cuda.synchronize()
+    cast_bytes = R * C * 2 + R * C + R * G * 4          # read bf16, write fp8 + scale_inv
+    deq_bytes = R * C + R * G * 4 + R * C * 2           # read fp8 + scale_inv, write bf16
+    step_bytes = cast_bytes + deq_bytes
+
+    def step(i, evs=None):
+        b = sets[i % NSETS]
+        if evs is not None:
+            evs[0].record(st)
+        fq.fp8q_cast_per_group128(b["x"], b["q"], b["s"], "e4m3fn", stream=st)
+        if evs is not None:
+            evs[1].record(st)
+        fq.fp8q_dequant_per_group128(b["q"], b["s"], b["y"], "e4m3fn", stream=st)
+        if evs is not None:
+            evs[2].record(st)
+
+    # ------------------------------------------------------------------ main loop
+    log(f"warmup {args.warmup}, timed {args.steps} steps")
+    with torch.cuda.stream(st):
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(i, evs[i])
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    cast_us = [evs[i][0].elapsed_time(evs[i][1]) * 1e3 for i in range(args.steps)]
+    deq_us = [evs[i][1].elapsed_time(evs[i][2]) * 1e3 for i in range(args.steps)]
+    cast_avg = float(np.mean(cast_us))
+    deq_avg = float(np.mean(deq_us))
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    cast_gbps = cast_bytes / (cast_avg * 1e-6) / 1e9
+    log(f"step {ms_per_step * 1e3:.1f} us  cast {cast_avg:.1f} us ({cast_gbps:.0f} GB/s)  "
+        f"dequant {deq_avg:.1f} us ({deq_bytes / (deq_avg * 1e-6) / 1e9:.0f} GB/s)")
+
+    rows = {
+        "group128_cast_bf16_e4m3fn_16384x7168": _row(cast_bytes, cast_us, R * C),
+        "group128_dequant_e4m3fn_bf16_16384x7168": _row(deq_bytes, deq_us, R * C),
+    }
+
+    # ------------------------------------------------------------------ copy calibration
+    # a plain device copy of known size: the reference for the HBM counters and a
+    # practical ceiling (reported as context, not as the roofline peak)
+    cp_n = 256 << 20
+    a = torch.empty(cp_n, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    with torch.cuda.stream(st):
+        for _ in range(3):
+            b.copy_(a)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(10):
+            b.copy_(a)
+        e1.record(st)
+    torch.cuda.synchronize()
+    copy_us = e0.elapsed_time(e1) * 1e3 / 10
+    copy_gbps = 2 * cp_n / (copy_us * 1e-6) / 1e9
+    del a, b
+    del sets, x0
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------------ other rows
+    if not args.no_rows:
+        rows.update(_other_rows(fq, W, np, torch, dev, st, args.rows_iters, log))
+
+    # ------------------------------------------------------------------ CPU oracle
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = _cpu_baseline(xh, R, C, G, log)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "per-128-group quantize + dequant round trip: bf16 [16384, 7168] (N(0,1), 7 channels x50) "
+                        "-> e4m3fn [16384, 7168] + float32 scale_inv [16384, 56] -> bf16 [16384, 7168]",
+            "rows": R, "cols": C, "fp8_format": "e4m3fn", "input": "bf16", "output": "bf16",
+            "bytes_per_step": step_bytes, "elements_per_s": round(2 * R * C / (ms_per_step * 1e-3), 1),
+            "percent_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+            "buffer_sets_rotated": NSETS,
+        },
+        "roofline": {
+            "kernel": "k_group128_v (fp8q_cast_per_group128)",
+            "bound": "hbm",
+            "achieved": round(cast_gbps, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(cast_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "avg_launch_us": round(cast_avg, 3),
+            "algorithmic_bytes_per_launch": cast_bytes,
+        },
+        "copy_reference": {"bytes": 2 * cp_n, "us": round(copy_us, 3), "gbps": round(copy_gbps, 1)},
+        "cpu_baseline": cpu,
+        "rows": rows,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def _row(nbytes, us_list, elems):
+    import numpy as np
+    avg = float(np.mean(us_list))
+    gbps = nbytes / (avg * 1e-6) / 1e9
+    return {"bytes": int(nbytes), "avg_us": round(avg, 3), "min_us": round(float(np.min(us_list)), 3),
+            "gbps": round(gbps, 1), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+            "elements_per_s": round(elems / (avg * 1e-6), 1)}
+
+
+def _other_rows(fq, W, np, torch, dev, st, iters, log):
+    """Each remaining hot-path operation on its own workload; a 1 GiB fill
+    between iterations (outside the events) evicts the Infinity Cache."""
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    out = {}
+
+    def timed(name, nbytes, elems, fn):
+        with torch.cuda.stream(st):
+            fn()
+            fn()
+            us = []
+            for _ in range(iters):
+                flush.fill_(1)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(st)
+                fn()
+                e1.record(st)
+                e1.synchronize()
+                us.append(e0.elapsed_time(e1) * 1e3)
+        out[name] = _row(nbytes, us, elems)
+        log(f"{name}: {out[name]['avg_us']} us, {out[name]['gbps']} GB/s")
+
+    # 128x128 block weight dequant: e4m3fn [18432, 7168] + float32 [144, 56] -> bf16
+    log("block weight workload")
+    ch, sh = W.block_weight()
+    M, N = ch.shape
+    qd = torch.from_numpy(ch).to(dev)
+    sd = torch.from_numpy(sh).to(dev)
+    yd = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    timed("block128_dequant_e4m3fn_bf16_18432x7168", M * N + sd.numel() * 4 + M * N * 2, M * N,
+          lambda: fq.fp8q_weight_dequant_block128(qd, sd, yd, "e4m3fn", stream=st))
+    del qd, sd, yd, ch
+
+    # per-tensor e5m2 on the 1-D gradient payload bf16 [2^28]
+    log("gradient payload workload")
+    n = 1 << 28
+    gh = W.gradient_payload(n=n)
+    gd = torch.from_numpy(gh).view(torch.int16).view(torch.bfloat16).to(dev)
+    del gh
+    amax = torch.empty(4, dtype=torch.float32, device=dev)
+    qg = torch.empty(n, dtype=torch.uint8, device=dev)
+    sg = torch.empty(1, dtype=torch.float32, device=dev)
+    ws = torch.empty(4, dtype=torch.int32, device=dev)
+    yg = torch.empty(n, dtype=torch.float32, device=dev)
+    timed("amax_bf16_268435456", n * 2 + 4, n, lambda: fq.fp8q_amax(gd, amax, stream=st))
+    timed("per_tensor_cast_bf16_e5m2_268435456 (amax pass + cast pass)", 2 * n * 2 + n + 4, n,
+          lambda: fq.fp8q_cast_per_tensor(gd, qg, sg, ws, "e5m2", stream=st))
+    timed("per_tensor_dequant_e5m2_f32_268435456", n + 4 + n * 4, n,
+          lambda: fq.fp8q_dequant_per_tensor(qg, sg, yg, "e5m2", stream=st))
+    del gd, qg, yg
+
+    # per-tensor and per-channel on [4096, 4096] fp32 / bf16 with row scales 10**U(-3,3)
+    log("row-scaled [4096, 4096] workload")
+    xf, xb, _ = W.tensor_rows_scaled()
+    R, C = xf.shape
+    for dt, xhost in (("f32", xf), ("bf16", xb)):
+        if dt == "f32":
+            xd = torch.from_numpy(xhost).to(dev)
+            esz = 4
+        else:
+            xd = torch.from_numpy(xhost).view(torch.int16).view(torch.bfloat16).to(dev)
+            esz = 2
+        q = torch.empty((R, C), dtype=torch.uint8, device=dev)
+        s1 = torch.empty(1, dtype=torch.float32, device=dev)
+        sr = torch.empty(R, dtype=torch.float32, device=dev)
+        y = torch.empty((R, C), dtype=xd.dtype, device=dev)
+        timed(f"per_tensor_cast_{dt}_e4m3fn_4096x4096 (2 passes)", 2 * R * C * esz + R * C + 4, R * C,
+              lambda: fq.fp8q_cast_per_tensor(xd, q, s1, ws, "e4m3fn", stream=st))
+        timed(f"per_tensor_dequant_e4m3fn_{dt}_4096x4096", R * C + 4 + R * C * esz, R * C,
+              lambda: fq.fp8q_dequant_per_tensor(q, s1, y, "e4m3fn", stream=st))
+        timed(f"per_channel_cast_{dt}_e4m3fn_4096x4096", R * C * esz + R * C + R * 4, R * C,
+              lambda: fq.fp8q_cast_per_channel(xd, q, sr, "e4m3fn", stream=st))
+        timed(f"per_channel_dequant_e4m3fn_{dt}_4096x4096", R * C + R * 4 + R * C * esz, R * C,
+              lambda: fq.fp8q_dequant_per_channel(q, sr, y, "e4m3fn", stream=st))
+        del xd, q, y
+    del flush
+    torch.cuda.empty_cache()
+    return out
+
+
+def _cpu_baseline(xh, R, C, G, log):
+    """The oracle, as written (single-threaded C), on row blocks of the same
+    activation workload: per-group cast then per-group dequant back to bf16,
+    until the whole tensor is done or about 20 s have passed."""
+    import numpy as np
+
+    import oracle
+    oracle.build(force=False)
+    L = oracle.default()
+    rows_done, t_total = 0, 0.0
+    blk = 1024
+    log("CPU oracle baseline")
+    while rows_done < R and t_total < 20.0:
+        xb = xh[rows_done:rows_done + blk]
+        t0 = time.perf_counter()
+        q, s = L.cast_per_group128(xb, "bf16", "e4m3fn")
+        L.dequant_per_group128(q, "e4m3fn", s, "bf16")
+        t_total += time.perf_counter() - t0
+        rows_done += xb.shape[0]
+    step_bytes_per_row = C * 2 + C + G * 4 + C + G * 4 + C * 2
+    gbps = rows_done * step_bytes_per_row / t_total / 1e9
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    log(f"CPU oracle: {rows_done} rows in {t_total:.1f} s -> {gbps:.3f} GB/s")
+    return {"value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows_done} of {R} rows of the activation workload (bf16 [{rows_done}, {C}]), "
+                      f"per-group cast + dequant round trip, {t_total:.1f} s single-threaded",
+            "cpu_model": cpu_model, "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+if __name__ == "__main__":
+    main()

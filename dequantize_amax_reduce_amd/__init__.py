@@ -1,0 +1,307 @@
+"""FP8 scaled cast for AMD Instinct MI355X: Python binding of libfp8q.so.
+
+Every step of quantize and dequantize runs in the HIP kernels of
+``csrc/fp8q_kernels.hip`` behind the C ABI of ``include/fp8q.h``; this module
+only marshals torch tensors (device memory) and the current HIP stream into
+those calls.  There is no CPU or PyTorch fallback: importing the package fails
+if the library is not built (``python -m dequantize_amax_reduce_amd.build``).
+
+Two layers:
+
+* ``fp8q_*`` -- one function per C entry point, same name, caller-allocated
+  outputs, returns None or raises (TypeError for FP8Q_EDTYPE, ValueError for
+  FP8Q_ESHAPE / FP8Q_EINVAL / FP8Q_EALIGN, RuntimeError for FP8Q_EHIP).
+* page-level helpers that allocate outputs with torch, mirroring the
+  functions the method is defined by: ``cast_to_fp8`` / ``cast_from_fp8``
+  (ColossalAI fp8.py), ``per_token_cast_to_fp8`` / ``per_token_cast_back``
+  (DeepEP "5 Utils") and ``weight_dequant`` (CSDN fp8_cast_bf16 notes).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfp8q.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "fp8q.h")
+
+E4M3FN, E5M2 = 0, 1
+F32, BF16, F16 = 0, 1, 2
+OK, EINVAL, EDTYPE, ESHAPE, EALIGN, EHIP = range(6)
+
+_FMT = {"e4m3": E4M3FN, "e4m3fn": E4M3FN, "e5m2": E5M2, E4M3FN: E4M3FN, E5M2: E5M2,
+        torch.float8_e4m3fn: E4M3FN, torch.float8_e5m2: E5M2}
+_FP8_DTYPE = {E4M3FN: torch.float8_e4m3fn, E5M2: torch.float8_e5m2}
+_DT = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m dequantize_amax_reduce_amd.build` "
+                          "(the HIP library is required; there is no fallback)")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    sigs = {
+        "fp8q_abi_version": (I, []),
+        "fp8q_status_str": (ctypes.c_char_p, [I]),
+        "fp8q_per_tensor_workspace_bytes": (ctypes.c_size_t, []),
+        "fp8q_amax": (I, [P, I, I64, P, P]),
+        "fp8q_cast_per_tensor": (I, [P, I, I64, I, P, P, P, P]),
+        "fp8q_cast_per_channel": (I, [P, I, I64, I64, I, P, P, P]),
+        "fp8q_cast_per_group128": (I, [P, I, I64, I64, I, P, P, P]),
+        "fp8q_dequant_per_tensor": (I, [P, I, I64, P, P, I, P]),
+        "fp8q_dequant_per_channel": (I, [P, I, I64, I64, P, P, I, P]),
+        "fp8q_dequant_per_group128": (I, [P, I, I64, I64, P, P, I, P]),
+        "fp8q_weight_dequant_block128": (I, [P, I, I64, I64, P, P, I, P]),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    return L
+
+
+lib = _load()
+ABI_FUNCTIONS = ("fp8q_abi_version", "fp8q_status_str", "fp8q_per_tensor_workspace_bytes", "fp8q_amax",
+                 "fp8q_cast_per_tensor", "fp8q_cast_per_channel", "fp8q_cast_per_group128",
+                 "fp8q_dequant_per_tensor", "fp8q_dequant_per_channel", "fp8q_dequant_per_group128",
+                 "fp8q_weight_dequant_block128")
+
+
+def header_functions() -> list:
+    """Names of the functions include/fp8q.h declares."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:fp8q_status_t|int|size_t|const char\*)\s+(fp8q_\w+)\s*\(",
+                                 text, re.M)))
+
+
+class Fp8qError(RuntimeError):
+    pass
+
+
+def _check(status: int, what: str):
+    if status == OK:
+        return
+    msg = f"{what}: {lib.fp8q_status_str(status).decode()}"
+    if status == EDTYPE:
+        raise TypeError(msg)
+    if status in (EINVAL, ESHAPE, EALIGN):
+        raise ValueError(msg)
+    raise Fp8qError(msg)
+
+
+# ---------------------------------------------------------------------------
+# marshalling
+# ---------------------------------------------------------------------------
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.numel() > 0:
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on a GPU (got {t.device})")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr() if t.numel() > 0 else 0
+
+
+def _stream(t: torch.Tensor, stream):
+    if stream is not None:
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    if t.device.type == "cuda":
+        return torch.cuda.current_stream(t.device).cuda_stream
+    return None
+
+
+def _hp_dtype(t: torch.Tensor, name: str) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"{name}: only float32, bfloat16 and float16 are supported (got {t.dtype})")
+    return _DT[t.dtype]
+
+
+def _fmt(fmt) -> int:
+    if fmt not in _FMT:
+        raise TypeError(f"unknown fp8 format {fmt!r} (use 'e4m3fn'/'e4m3' or 'e5m2')")
+    return _FMT[fmt]
+
+
+def _fp8(t: torch.Tensor, fmt, name: str) -> int:
+    """fp8 tensors may be float8_e4m3fn / float8_e5m2 or uint8 codes."""
+    if t.dtype in (torch.float8_e4m3fn, torch.float8_e5m2):
+        if fmt is not None and _fmt(fmt) != _FMT[t.dtype]:
+            raise TypeError(f"{name} is {t.dtype} but fmt={fmt!r}")
+        return _FMT[t.dtype]
+    if t.dtype != torch.uint8:
+        raise TypeError(f"{name} must be float8_e4m3fn, float8_e5m2 or uint8 codes (got {t.dtype})")
+    return _fmt("e4m3fn" if fmt is None else fmt)
+
+
+def _rows_cols(t: torch.Tensor):
+    if t.dim() == 0:
+        return 1, 1
+    cols = t.shape[-1]
+    rows = t.numel() // cols if cols else (t.numel() if t.dim() == 1 else int(torch.tensor(t.shape[:-1]).prod()))
+    return rows, cols
+
+
+# ---------------------------------------------------------------------------
+# one function per C entry point
+# ---------------------------------------------------------------------------
+
+def fp8q_abi_version() -> int:
+    return lib.fp8q_abi_version()
+
+
+def fp8q_status_str(status: int) -> str:
+    return lib.fp8q_status_str(status).decode()
+
+
+def fp8q_per_tensor_workspace_bytes() -> int:
+    return lib.fp8q_per_tensor_workspace_bytes()
+
+
+def fp8q_amax(x: torch.Tensor, amax: torch.Tensor, stream=None) -> None:
+    if amax.dtype != torch.float32 or amax.numel() < 1:
+        raise TypeError("amax must be a float32 tensor with at least one element")
+    _check(lib.fp8q_amax(_dev(x, "x"), _hp_dtype(x, "x"), x.numel(), _dev(amax, "amax"), _stream(x, stream)),
+           "fp8q_amax")
+
+
+def fp8q_cast_per_tensor(x, q, scale_inv, workspace, fmt="e4m3fn", stream=None) -> None:
+    f = _fp8(q, fmt, "q")
+    if q.numel() != x.numel() or scale_inv.dtype != torch.float32 or scale_inv.numel() < 1:
+        raise ValueError("fp8q_cast_per_tensor: q must match x and scale_inv must be float32[1]")
+    if workspace.numel() * workspace.element_size() < fp8q_per_tensor_workspace_bytes():
+        raise ValueError("fp8q_cast_per_tensor: workspace too small")
+    _check(lib.fp8q_cast_per_tensor(_dev(x, "x"), _hp_dtype(x, "x"), x.numel(), f, _dev(q, "q"),
+                                    _dev(scale_inv, "scale_inv"), _dev(workspace, "workspace"),
+                                    _stream(x, stream)), "fp8q_cast_per_tensor")
+
+
+def fp8q_cast_per_channel(x, q, scale_inv, fmt="e4m3fn", stream=None) -> None:
+    f = _fp8(q, fmt, "q")
+    rows, cols = _rows_cols(x)
+    if q.numel() != x.numel() or scale_inv.dtype != torch.float32 or scale_inv.numel() != rows:
+        raise ValueError("fp8q_cast_per_channel: q must match x and scale_inv must be float32[rows]")
+    _check(lib.fp8q_cast_per_channel(_dev(x, "x"), _hp_dtype(x, "x"), rows, cols, f, _dev(q, "q"),
+                                     _dev(scale_inv, "scale_inv"), _stream(x, stream)), "fp8q_cast_per_channel")
+
+
+def fp8q_cast_per_group128(x, q, scale_inv, fmt="e4m3fn", stream=None) -> None:
+    f = _fp8(q, fmt, "q")
+    rows, cols = _rows_cols(x)
+    if q.numel() != x.numel() or scale_inv.dtype != torch.float32 or \
+            (cols % 128 == 0 and scale_inv.numel() != rows * (cols // 128)):
+        raise ValueError("fp8q_cast_per_group128: q must match x and scale_inv must be float32[rows, cols/128]")
+    _check(lib.fp8q_cast_per_group128(_dev(x, "x"), _hp_dtype(x, "x"), rows, cols, f, _dev(q, "q"),
+                                      _dev(scale_inv, "scale_inv"), _stream(x, stream)), "fp8q_cast_per_group128")
+
+
+def fp8q_dequant_per_tensor(q, scale_inv, y, fmt=None, stream=None) -> None:
+    f = _fp8(q, fmt, "q")
+    if y.numel() != q.numel() or scale_inv.dtype != torch.float32:
+        raise ValueError("fp8q_dequant_per_tensor: y must match q and scale_inv must be float32[1]")
+    _check(lib.fp8q_dequant_per_tensor(_dev(q, "q"), f, q.numel(), _dev(scale_inv, "scale_inv"), _dev(y, "y"),
+                                       _hp_dtype(y, "y"), _stream(q, stream)), "fp8q_dequant_per_tensor")
+
+
+def fp8q_dequant_per_channel(q, scale_inv, y, fmt=None, stream=None) -> None:
+    f = _fp8(q, fmt, "q")
+    rows, cols = _rows_cols(q)
+    if y.numel() != q.numel() or scale_inv.dtype != torch.float32 or scale_inv.numel() != rows:
+        raise ValueError("fp8q_dequant_per_channel: y must match q and scale_inv must be float32[rows]")
+    _check(lib.fp8q_dequant_per_channel(_dev(q, "q"), f, rows, cols, _dev(scale_inv, "scale_inv"), _dev(y, "y"),
+                                        _hp_dtype(y, "y"), _stream(q, stream)), "fp8q_dequant_per_channel")
+
+
+def fp8q_dequant_per_group128(q, scale_inv, y, fmt=None, stream=None) -> None:
+    f = _fp8(q, fmt, "q")
+    rows, cols = _rows_cols(q)
+    if y.numel() != q.numel() or scale_inv.dtype != torch.float32 or \
+            (cols % 128 == 0 and scale_inv.numel() != rows * (cols // 128)):
+        raise ValueError("fp8q_dequant_per_group128: y must match q and scale_inv must be float32[rows, cols/128]")
+    _check(lib.fp8q_dequant_per_group128(_dev(q, "q"), f, rows, cols, _dev(scale_inv, "scale_inv"), _dev(y, "y"),
+                                         _hp_dtype(y, "y"), _stream(q, stream)), "fp8q_dequant_per_group128")
+
+
+def fp8q_weight_dequant_block128(q, scale_inv, y, fmt=None, stream=None) -> None:
+    f = _fp8(q, fmt, "q")
+    if q.dim() != 2 or scale_inv.dim() != 2:
+        raise ValueError("fp8q_weight_dequant_block128: q and scale_inv must be 2-D")
+    M, N = q.shape
+    if tuple(scale_inv.shape) != ((M + 127) // 128, (N + 127) // 128) or scale_inv.dtype != torch.float32:
+        raise ValueError("fp8q_weight_dequant_block128: scale_inv must be float32[ceil(M/128), ceil(N/128)]")
+    if y.numel() != q.numel():
+        raise ValueError("fp8q_weight_dequant_block128: y must match q")
+    _check(lib.fp8q_weight_dequant_block128(_dev(q, "q"), f, M, N, _dev(scale_inv, "scale_inv"), _dev(y, "y"),
+                                            _hp_dtype(y, "y"), _stream(q, stream)),
+           "fp8q_weight_dequant_block128")
+
+
+# ---------------------------------------------------------------------------
+# page-level helpers (allocate outputs with torch; all compute in the kernels)
+# ---------------------------------------------------------------------------
+
+def cast_to_fp8(inp: torch.Tensor, fp8_format="e4m3", per_channel_scale=False):
+    """(fp8 tensor, scale_inv) -- ColossalAI fp8.py cast_to_fp8.  scale_inv is
+    float32[1] per-tensor or float32[rows] per-channel (row-indexed)."""
+    f = _fmt(fp8_format)
+    _hp_dtype(inp, "inp")
+    q = torch.empty(inp.shape, dtype=_FP8_DTYPE[f], device=inp.device)
+    if per_channel_scale:
+        rows, _ = _rows_cols(inp)
+        sinv = torch.empty(rows, dtype=torch.float32, device=inp.device)
+        fp8q_cast_per_channel(inp, q, sinv, f)
+    else:
+        sinv = torch.empty(1, dtype=torch.float32, device=inp.device)
+        ws = torch.empty(fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32, device=inp.device)
+        fp8q_cast_per_tensor(inp, q, sinv, ws, f)
+    return q, sinv
+
+
+def cast_from_fp8(inp: torch.Tensor, scale_inv: torch.Tensor, ret_type: torch.dtype, per_channel_scale=False):
+    """ColossalAI fp8.py cast_from_fp8: ret_type(fp32(inp) * scale_inv)."""
+    if inp.dtype not in (torch.float8_e4m3fn, torch.float8_e5m2):
+        raise TypeError("Only float8_e4m3fn and float8_e5m2 are allowed.")
+    y = torch.empty(inp.shape, dtype=ret_type, device=inp.device)
+    if per_channel_scale:
+        fp8q_dequant_per_channel(inp, scale_inv.reshape(-1), y)
+    else:
+        fp8q_dequant_per_tensor(inp, scale_inv.reshape(-1), y)
+    return y
+
+
+def per_token_cast_to_fp8(x: torch.Tensor, fp8_format="e4m3fn"):
+    """DeepEP per_token_cast_to_fp8: x [m, n], n % 128 == 0 ->
+    (fp8 [m, n], scale_inv float32 [m, n/128])."""
+    if x.dim() != 2 or x.size(1) % 128 != 0:
+        raise ValueError("per_token_cast_to_fp8: x must be 2-D with x.size(1) % 128 == 0")
+    f = _fmt(fp8_format)
+    m, n = x.shape
+    q = torch.empty((m, n), dtype=_FP8_DTYPE[f], device=x.device)
+    sinv = torch.empty((m, n // 128), dtype=torch.float32, device=x.device)
+    fp8q_cast_per_group128(x, q, sinv, f)
+    return q, sinv
+
+
+def per_token_cast_back(q: torch.Tensor, scale_inv: torch.Tensor, ret_type=torch.bfloat16):
+    """Inverse of per_token_cast_to_fp8: ret_type(fp32(q) * scale_inv[r, c // 128])."""
+    y = torch.empty(q.shape, dtype=ret_type, device=q.device)
+    fp8q_dequant_per_group128(q, scale_inv, y)
+    return y
+
+
+def weight_dequant(x: torch.Tensor, s: torch.Tensor, block_size: int = 128, ret_type=torch.bfloat16):
+    """CSDN fp8_cast_bf16 notes, weight_dequant: x [M, N] fp8 with s
+    [ceil(M/128), ceil(N/128)] -> ret_type (bf16, the page's default dtype)."""
+    if block_size != 128:
+        raise ValueError("weight_dequant: only block_size=128 is implemented")
+    if x.dim() != 2 or s.dim() != 2:
+        raise ValueError("Input tensors must have 2 dimensions")
+    y = torch.empty(x.shape, dtype=ret_type, device=x.device)
+    fp8q_weight_dequant_block128(x, s, y)
+    return y

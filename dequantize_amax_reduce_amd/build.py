@@ -1,0 +1,55 @@
+"""Build the HIP library libfp8q.so in-tree with hipcc for gfx950.
+
+    python -m dequantize_amax_reduce_amd.build
+
+Flags that matter for the numerics:
+  -ffp-contract=off   no FMA contraction of the binary32 products
+  -Xclang -target-feature -Xclang -packed-fp32-ops
+                      no v_pk_{add,mul,fma}_f32 (scalar VALU fp32 only)
+  no -ffast-math / -fgpu-flush-denormals-to-zero: IEEE division and fp32
+  denormals stay on (correctly rounded scale = fp8_max / amax).
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libfp8q.so")
+SOURCES = [os.path.join(CSRC, "fp8q_kernels.hip"), os.path.join(CSRC, "fp8q_abi.cpp")]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found (ROCm is required to build libfp8q.so)")
+
+
+def build(verbose: bool = False) -> str:
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+           "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-Wall", "-I", INCLUDE, "-I", CSRC, *SOURCES, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    # the host pass does not know the device-only feature name; that warning is expected
+    noise = "'-packed-fp32-ops' is not a recognized feature"
+    msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{msgs}")
+    if msgs.strip() and verbose:
+        print(msgs)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,160 @@
+/*
+ * fp8q.h -- C ABI of the FP8 scaled-cast library (quantize: amax -> scale ->
+ * cast to fp8; dequantize: fp8 x scale_inv) for AMD Instinct MI355X (gfx950).
+ *
+ * Conventions for every entry point
+ *  - Pointers named x, q, y, scale_inv, amax and workspace are DEVICE pointers
+ *    owned by the caller.  Tensors are dense, contiguous and row-major.
+ *  - The library allocates nothing, keeps no pointer after returning, holds no
+ *    mutable global state and is re-entrant.
+ *  - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
+ *    NULL means the default stream).  Inputs must stay valid and unchanged,
+ *    and outputs untouched by others, until the stream reaches the work.
+ *    Kernel faults surface at the caller's next synchronisation.
+ *  - Arguments are validated on the host before any HIP call; a call that
+ *    returns an error other than FP8Q_EHIP has enqueued nothing.
+ *  - fp8 tensors are uint8 codes of the OCP 8-bit formats: E4M3 ("e4m3fn":
+ *    bias 7, no infinities, max 448) or E5M2 (bias 15, IEEE-like, max 57344).
+ *  - Sizes are int64 element counts; rows * cols must not overflow int64.
+ *
+ * Numerics (identical on every path and launch shape)
+ *  - amax = max |x| exactly (a max is order-independent); NaN propagates.
+ *  - scale and scale_inv are binary32 results of correctly rounded divisions;
+ *    products are single binary32 multiplies (no FMA, no reciprocal-multiply).
+ *  - fp32 -> fp8 rounds to nearest, ties to even; magnitudes that round above
+ *    the format maximum (and +-inf) saturate to +-max; the sign of zero is
+ *    kept; NaN encodes as S.1111111.
+ *  - fp32 -> bf16 / fp16 outputs round to nearest even (fp16 overflows to inf).
+ *
+ * Sources: ColossalAI `colossalai/quantization/fp8.py` (cast_to_fp8,
+ * cast_from_fp8); DeepEP utils notes "5 Utils" (per_token_cast_to_fp8); CSDN
+ * notes "FP8 (8 bits) & FP16 (16 bits)" (weight_dequant,
+ * weight_dequant_kernel).
+ */
+#ifndef FP8Q_H
+#define FP8Q_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8Q_ABI_VERSION 1
+
+/* fp8 format: cast_to_fp8's fp8_format ("e4m3" -> float8_e4m3fn, "e5m2" -> float8_e5m2) */
+typedef enum { FP8Q_E4M3FN = 0, FP8Q_E5M2 = 1 } fp8q_fmt_t;
+
+/* element type of the high-precision side: cast_to_fp8 accepts float32,
+ * float16 and bfloat16; cast_from_fp8's ret_type picks the output type */
+typedef enum { FP8Q_F32 = 0, FP8Q_BF16 = 1, FP8Q_F16 = 2 } fp8q_dtype_t;
+
+typedef enum {
+    FP8Q_OK = 0,
+    FP8Q_EINVAL = 1, /* negative size, int64 overflow, NULL pointer with a non-empty
+                        size, NULL workspace, or overlapping input/output ranges */
+    FP8Q_EDTYPE = 2, /* unknown fp8 format or element type (cast_to_fp8 / cast_from_fp8
+                        raise TypeError for these) */
+    FP8Q_ESHAPE = 3, /* per-128-group with cols % 128 != 0 (per_token_cast_to_fp8's assert) */
+    FP8Q_EALIGN = 4, /* a pointer not aligned to its element size */
+    FP8Q_EHIP = 5    /* a kernel launch failed (hipGetLastError after the launch; an
+                        earlier unchecked error on the calling thread is reported too) */
+} fp8q_status_t;
+
+/* FP8Q_ABI_VERSION of the built library */
+int fp8q_abi_version(void);
+
+/* static, human-readable name of a status code (never NULL) */
+const char* fp8q_status_str(int status);
+
+/* bytes of device workspace fp8q_cast_per_tensor needs (4, rounded up to 16) */
+size_t fp8q_per_tensor_workspace_bytes(void);
+
+/*
+ * Global amax (ColossalAI fp8.py, cast_to_fp8, per-tensor branch:
+ * inp.abs().max().float()).  Writes max_i |x_i| over n elements to amax[0]
+ * (one binary32, device memory, 4-byte aligned); NaN anywhere gives a NaN;
+ * n == 0 gives +0.  Two stages: a per-workgroup reduction, then an atomic max
+ * on the binary32 bits into amax[0], which the call first clears on `stream`.
+ */
+fp8q_status_t fp8q_amax(const void* x, int xdtype, int64_t n, float* amax, void* stream);
+
+/*
+ * Per-tensor cast (ColossalAI fp8.py, cast_to_fp8 with per_channel_scale=False).
+ *   amax = max |x|; a = amax > 0 ? amax : 1 (NaN also gives 1);
+ *   scale = fp8_max / a; scale_inv[0] = 1 / scale; q[i] = fp8(fp32(x[i]) * scale).
+ * x: n elements of xdtype; q: n bytes; scale_inv: 1 float; workspace: at least
+ * fp8q_per_tensor_workspace_bytes() bytes, 4-byte aligned, caller-owned, not
+ * shared with a concurrent call.  n == 0 writes scale_inv[0] = 1.0 and nothing
+ * else (cast_to_fp8's empty-tensor branch).  Reads x twice (amax pass, then
+ * the scale-and-cast pass).
+ */
+fp8q_status_t fp8q_cast_per_tensor(const void* x, int xdtype, int64_t n, int fmt,
+                                   uint8_t* q, float* scale_inv, void* workspace, void* stream);
+
+/*
+ * Per-channel cast (ColossalAI fp8.py, cast_to_fp8 with per_channel_scale=True;
+ * the channel is the last dimension, so one row of x [rows, cols]).
+ *   amax_r = max_c |x[r, c]|; a_r = amax_r > 0 ? amax_r : 1;
+ *   scale_r = fp8_max / a_r; scale_inv[r] = a_r / fp8_max (not 1 / scale_r);
+ *   q[r, c] = fp8(fp32(x[r, c]) * scale_r).
+ * scale_inv has `rows` floats (row-indexed).  rows == 0 is a no-op; cols == 0
+ * writes scale_inv[r] = 1.0 for every row (the empty-tensor branch).
+ */
+fp8q_status_t fp8q_cast_per_channel(const void* x, int xdtype, int64_t rows, int64_t cols, int fmt,
+                                    uint8_t* q, float* scale_inv, void* stream);
+
+/*
+ * Per-128-group cast (DeepEP "5 Utils", per_token_cast_to_fp8: x viewed as
+ * [rows, cols/128, 128]).  For every row r and group g (columns 128g..128g+127):
+ *   amax = max(max |x|, 1e-4) (binary32 0x38D1B717; NaN propagates);
+ *   scale = fp8_max / amax; scale_inv[r, g] = amax / fp8_max;
+ *   q = fp8(fp32(x) * scale).
+ * fp8_max is 448 for E4M3 (the page's constant) and 57344 for E5M2.
+ * cols % 128 != 0 -> FP8Q_ESHAPE.  scale_inv is [rows, cols/128] row-major.
+ * rows == 0 or cols == 0 is a no-op.
+ */
+fp8q_status_t fp8q_cast_per_group128(const void* x, int xdtype, int64_t rows, int64_t cols, int fmt,
+                                     uint8_t* q, float* scale_inv, void* stream);
+
+/*
+ * Per-tensor dequant (ColossalAI fp8.py, cast_from_fp8, per-tensor):
+ *   y[i] = ydtype(fp32(q[i]) * scale_inv[0]) -- the binary32 product rounded
+ * once more to bf16/fp16 when ydtype is not F32.  n == 0 is a no-op.
+ */
+fp8q_status_t fp8q_dequant_per_tensor(const uint8_t* q, int fmt, int64_t n, const float* scale_inv,
+                                      void* y, int ydtype, void* stream);
+
+/*
+ * Per-channel dequant (ColossalAI fp8.py, cast_from_fp8, per_channel_scale=True):
+ *   y[r, c] = ydtype(fp32(q[r, c]) * scale_inv[r]); scale_inv has `rows` floats.
+ */
+fp8q_status_t fp8q_dequant_per_channel(const uint8_t* q, int fmt, int64_t rows, int64_t cols,
+                                       const float* scale_inv, void* y, int ydtype, void* stream);
+
+/*
+ * Per-128-group dequant, the inverse of per_token_cast_to_fp8 (DeepEP
+ * "5 Utils" names it per_token_cast_back without showing it; this is the
+ * plain reading, the same product as cast_from_fp8):
+ *   y[r, c] = ydtype(fp32(q[r, c]) * scale_inv[r, c / 128]).
+ * cols % 128 != 0 -> FP8Q_ESHAPE.
+ */
+fp8q_status_t fp8q_dequant_per_group128(const uint8_t* q, int fmt, int64_t rows, int64_t cols,
+                                        const float* scale_inv, void* y, int ydtype, void* stream);
+
+/*
+ * 128x128 block weight dequant (CSDN "FP8 (8 bits) & FP16 (16 bits)",
+ * weight_dequant and weight_dequant_kernel): q is [M, N]; scale_inv is
+ * [ceil(M/128), ceil(N/128)] row-major; partial edge tiles are masked;
+ *   y[i, j] = ydtype(fp32(q[i, j]) * scale_inv[(i/128) * ceil(N/128) + j/128]).
+ * The page stores the product into a bf16 buffer (the default dtype), which
+ * is ydtype = FP8Q_BF16; F32 and F16 outputs are also offered.
+ */
+fp8q_status_t fp8q_weight_dequant_block128(const uint8_t* q, int fmt, int64_t M, int64_t N,
+                                           const float* scale_inv, void* y, int ydtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP8Q_H */

@@ -1,0 +1,99 @@
+"""CPU tests of the C ABI boundary: the HIP library loads without a GPU,
+exports every function include/fp8q.h declares, and every argument error is
+reported before any HIP call (these calls enqueue nothing, so they need no
+GPU).  Fake device addresses are never dereferenced on these paths."""
+import ctypes
+import re
+import subprocess
+
+import pytest
+
+import dequantize_amax_reduce_amd as fq
+
+L = fq.lib
+P = lambda a: ctypes.c_void_p(a)          # a fake, never-dereferenced address
+A = 0x7F0000000000                          # 256-B aligned fake base
+E4, E5, F32, BF16, F16 = 0, 1, 0, 1, 2
+
+
+def test_exports_match_header():
+    declared = fq.header_functions()
+    assert set(declared) == set(fq.ABI_FUNCTIONS)
+    out = subprocess.run(["nm", "-D", "--defined-only", fq.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r" T (fp8q_\w+)$", out, re.M))
+    assert set(declared) <= exported, set(declared) - exported
+
+
+def test_version_and_strings():
+    assert L.fp8q_abi_version() == 1
+    for st in range(7):
+        assert L.fp8q_status_str(st)
+    assert L.fp8q_per_tensor_workspace_bytes() >= 4
+    assert L.fp8q_per_tensor_workspace_bytes() % 16 == 0
+
+
+def test_group128_errors():
+    f = L.fp8q_cast_per_group128
+    assert f(P(A), BF16, 4, 100, E4, P(A + 4096), P(A + 8192), None) == fq.ESHAPE
+    assert f(P(A), 7, 4, 128, E4, P(A + 4096), P(A + 8192), None) == fq.EDTYPE
+    assert f(P(A), BF16, 4, 128, 9, P(A + 4096), P(A + 8192), None) == fq.EDTYPE
+    assert f(P(A), BF16, -1, 128, E4, P(A + 4096), P(A + 8192), None) == fq.EINVAL
+    assert f(None, BF16, 4, 128, E4, P(A + 4096), P(A + 8192), None) == fq.EINVAL
+    assert f(P(A), BF16, 4, 128, E4, None, P(A + 8192), None) == fq.EINVAL
+    assert f(P(A), BF16, 4, 128, E4, P(A + 4096), None, None) == fq.EINVAL
+    assert f(P(A + 1), BF16, 4, 128, E4, P(A + 4096), P(A + 8192), None) == fq.EALIGN
+    assert f(P(A), F32, 4, 128, E4, P(A + 4096), P(A + 8194), None) == fq.EALIGN
+    assert f(P(A), BF16, 4, 128, E4, P(A + 512), P(A + 8192), None) == fq.EINVAL      # x/q overlap
+    assert f(P(A), BF16, 4, 128, E4, P(A + 4096), P(A + 4096 + 500), None) == fq.EINVAL  # q/s overlap
+    assert f(P(A), BF16, 2 ** 62, 2 ** 10, E4, P(A + 4096), P(A + 8192), None) == fq.EINVAL  # overflow
+    # empty shapes are valid no-ops that never touch the pointers
+    assert f(None, BF16, 0, 128, E4, None, None, None) == fq.OK
+    assert f(None, BF16, 5, 0, E4, None, None, None) == fq.OK
+
+
+def test_tensor_and_channel_errors():
+    t = L.fp8q_cast_per_tensor
+    assert t(P(A), BF16, 16, E4, P(A + 4096), P(A + 8192), None, None) == fq.EINVAL       # no workspace
+    assert t(P(A), BF16, 16, E4, P(A + 4096), P(A + 8192), P(A + 8194), None) == fq.EALIGN
+    assert t(P(A), BF16, 16, E4, P(A + 4096), P(A + 8192), P(A + 8192), None) == fq.EINVAL  # ws = scale_inv
+    assert t(P(A), 3, 16, E4, P(A + 4096), P(A + 8192), P(A + 9000), None) == fq.EDTYPE
+    assert t(P(A), BF16, -5, E4, P(A + 4096), P(A + 8192), P(A + 9000), None) == fq.EINVAL
+    c = L.fp8q_cast_per_channel
+    assert c(P(A), F32, 4, 16, E5, P(A + 4096), None, None) == fq.EINVAL
+    assert c(P(A + 2), F32, 4, 16, E5, P(A + 4096), P(A + 8192), None) == fq.EALIGN
+    assert c(P(A), F32, 4, -16, E5, P(A + 4096), P(A + 8192), None) == fq.EINVAL
+    assert c(None, F32, 0, 16, E5, None, None, None) == fq.OK
+    a = L.fp8q_amax
+    assert a(P(A), F32, 10, None, None) == fq.EINVAL
+    assert a(P(A), F32, 10, P(A + 2), None) == fq.EALIGN
+    assert a(P(A), F32, 10, P(A + 4), None) == fq.EINVAL                                   # overlap
+    assert a(P(A), 5, 10, P(A + 4096), None) == fq.EDTYPE
+
+
+def test_dequant_errors():
+    d = L.fp8q_dequant_per_tensor
+    assert d(P(A), E4, 16, None, P(A + 4096), BF16, None) == fq.EINVAL
+    assert d(P(A), E4, 16, P(A + 8192), P(A + 4097), BF16, None) == fq.EALIGN
+    assert d(P(A), E4, 16, P(A + 8192), P(A + 8), BF16, None) == fq.EINVAL                 # q/y overlap
+    assert d(P(A), 2, 16, P(A + 8192), P(A + 4096), BF16, None) == fq.EDTYPE
+    assert d(None, E4, 0, None, None, BF16, None) == fq.OK
+    g = L.fp8q_dequant_per_group128
+    assert g(P(A), E4, 4, 130, P(A + 8192), P(A + 4096 * 4), F32, None) == fq.ESHAPE
+    assert g(P(A), E4, 4, 128, P(A + 8193), P(A + 4096 * 4), F32, None) == fq.EALIGN
+    r = L.fp8q_dequant_per_channel
+    assert r(P(A), E4, 4, 16, P(A + 8192), P(A + 4096), 9, None) == fq.EDTYPE
+    b = L.fp8q_weight_dequant_block128
+    assert b(P(A), E4, -1, 16, P(A + 8192), P(A + 4096), BF16, None) == fq.EINVAL
+    assert b(P(A), E4, 2 ** 62, 2 ** 62, P(A + 8192), P(A + 4096), BF16, None) == fq.EINVAL
+    assert b(P(A), E4, 16, 16, None, P(A + 4096), BF16, None) == fq.EINVAL
+    assert b(None, E4, 0, 16, None, None, BF16, None) == fq.OK
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros((2, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fq.fp8q_cast_per_group128(x, torch.empty((2, 128), dtype=torch.uint8), torch.empty((2, 1)))
+    with pytest.raises(TypeError):
+        fq.cast_from_fp8(torch.zeros(4), torch.ones(1), torch.float32)
