@@ -176,13 +176,13 @@ def main():
             "buffer_sets_rotated": NSETS,
         },
         "roofline": {
-            "kernel": "k_group128_v (fp8q_cast_per_group128)",
+            "kernel": "k_group128 (fp8q_cast_per_group128)",
             "bound": "hbm",
             "achieved": round(cast_gbps, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(cast_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(),
             "avg_launch_us": round(cast_avg, 3),
             "algorithmic_bytes_per_launch": cast_bytes,
         },
@@ -191,6 +191,37 @@ def main():
         "rows": rows,
     }
     print(json.dumps(out), flush=True)
+
+
+KERNEL_SOURCES = ("dequantize_amax_reduce_amd/csrc/fp8q_device.h", "dequantize_amax_reduce_amd/csrc/fp8q_kernels.hip")
+TRAFFIC_SUMMARY = "profiles/k_group128__activation_16384x7168__hbm_traffic.md"
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(root, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the group-cast kernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None when that summary is
+    missing or was taken on different kernel sources."""
+    import re
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), TRAFFIC_SUMMARY)
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    src = re.search(r"^kernel_sources_sha256:\s*([0-9a-f]{64})", text, re.M)
+    val = re.search(r"^hbm_bytes_per_launch:\s*([0-9.]+)", text, re.M)
+    if not src or not val or src.group(1) != kernel_source_hash():
+        return None
+    return float(val.group(1))
 
 
 def _row(nbytes, us_list, elems):
@@ -203,9 +234,12 @@ def _row(nbytes, us_list, elems):
 
 
 def _other_rows(fq, W, np, torch, dev, st, iters, log):
-    """Each remaining hot-path operation on its own workload; a 1 GiB fill
-    between iterations (outside the events) evicts the Infinity Cache."""
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    """Each remaining hot-path operation on its own workload.  Between
+    iterations, outside the events, a 1 GiB read (a max-reduction) replaces the
+    256 MB Infinity Cache contents with clean lines, so inputs come from HBM
+    and no dirty lines from an earlier write are written back inside the
+    timed kernel."""
+    flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
     out = {}
 
     def timed(name, nbytes, elems, fn):
@@ -214,7 +248,7 @@ def _other_rows(fq, W, np, torch, dev, st, iters, log):
             fn()
             us = []
             for _ in range(iters):
-                flush.fill_(1)
+                flush.max()
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(st)
                 fn()
