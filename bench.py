@@ -10,8 +10,12 @@ re-read what the previous one left in the 256 MB Infinity Cache.
 
 `value` = algorithmic bytes of the step (every byte the method must read and
 write, scales included) / wall time per step, in GB/s.  HIP events recorded on
-the launch stream around each kernel give the per-kernel average duration
-used for the roofline of the dominant kernel (the group cast).  The other
+the launch stream give the per-kernel average duration used for the roofline
+of the dominant kernel (the group cast): one event before each cast and one
+between cast and dequant (the next step's first event closes the dequant).
+The events are created with hipEventDisableSystemFence: a timing-only event
+then skips the system-scope cache write-back and invalidate that a default
+event record performs, which otherwise adds about 3 us to every interval.  The other
 hot-path operations (block dequant, per-tensor, per-channel, amax) are timed
 on their own workloads after the main loop, with a cache flush between
 iterations outside the events, and reported under "rows".
@@ -30,6 +34,49 @@ import sys
 import time
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E peak, 8 TB/s
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+
+
+class HipEvents:
+    """Timing events of the HIP runtime that torch (and libfp8q.so) already
+    use in this process, created with hipEventDisableSystemFence."""
+
+    def __init__(self):
+        import ctypes
+        path = [l.split()[-1] for l in open("/proc/self/maps") if "libamdhip64" in l][0]
+        hip = ctypes.CDLL(path)
+        hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip, self.ct, self.pool = hip, ctypes, []
+
+    def new(self):
+        e = self.ct.c_void_p()
+        rc = self.hip.hipEventCreateWithFlags(self.ct.byref(e), HIP_EVENT_DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+        self.pool.append(e)
+        return e
+
+    def record(self, e, stream):
+        rc = self.hip.hipEventRecord(e, self.ct.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def us(self, a, b):
+        self.hip.hipEventSynchronize(b)
+        f = self.ct.c_float()
+        rc = self.hip.hipEventElapsedTime(self.ct.byref(f), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return f.value * 1e3
+
+    def close(self):
+        for e in self.pool:
+            self.hip.hipEventDestroy(e)
+        self.pool = []
 METRIC = "quantize/dequant GB/s and % of HBM peak, per-128-group bf16→e4m3"
 
 
@@ -85,33 +132,34 @@ def main():
     deq_bytes = R * C + R * G * 4 + R * C * 2           # read fp8 + scale_inv, write bf16
     step_bytes = cast_bytes + deq_bytes
 
-    def step(i, evs=None):
+    HE = HipEvents()
+
+    def step(i, ev_start=None, ev_mid=None):
         b = sets[i % NSETS]
-        if evs is not None:
-            evs[0].record(st)
+        if ev_start is not None:
+            HE.record(ev_start, st)
         fq.fp8q_cast_per_group128(b["x"], b["q"], b["s"], "e4m3fn", stream=st)
-        if evs is not None:
-            evs[1].record(st)
+        if ev_mid is not None:
+            HE.record(ev_mid, st)
         fq.fp8q_dequant_per_group128(b["q"], b["s"], b["y"], "e4m3fn", stream=st)
-        if evs is not None:
-            evs[2].record(st)
 
     # ------------------------------------------------------------------ main loop
     log(f"warmup {args.warmup}, timed {args.steps} steps")
+    ev_start = [HE.new() for _ in range(args.steps + 1)]
+    ev_mid = [HE.new() for _ in range(args.steps)]
     with torch.cuda.stream(st):
         for i in range(args.warmup):
             step(i)
         torch.cuda.synchronize()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-        torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(args.steps):
-            step(i, evs[i])
+            step(i, ev_start[i], ev_mid[i])
+        HE.record(ev_start[args.steps], st)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    cast_us = [evs[i][0].elapsed_time(evs[i][1]) * 1e3 for i in range(args.steps)]
-    deq_us = [evs[i][1].elapsed_time(evs[i][2]) * 1e3 for i in range(args.steps)]
+    cast_us = [HE.us(ev_start[i], ev_mid[i]) for i in range(args.steps)]
+    deq_us = [HE.us(ev_mid[i], ev_start[i + 1]) for i in range(args.steps)]
     cast_avg = float(np.mean(cast_us))
     deq_avg = float(np.mean(deq_us))
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -133,13 +181,13 @@ def main():
     with torch.cuda.stream(st):
         for _ in range(3):
             b.copy_(a)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(st)
+        e0, e1 = HE.new(), HE.new()
+        HE.record(e0, st)
         for _ in range(10):
             b.copy_(a)
-        e1.record(st)
+        HE.record(e1, st)
     torch.cuda.synchronize()
-    copy_us = e0.elapsed_time(e1) * 1e3 / 10
+    copy_us = HE.us(e0, e1) / 10
     copy_gbps = 2 * cp_n / (copy_us * 1e-6) / 1e9
     del a, b
     del sets, x0
@@ -147,7 +195,8 @@ def main():
 
     # ------------------------------------------------------------------ other rows
     if not args.no_rows:
-        rows.update(_other_rows(fq, W, np, torch, dev, st, args.rows_iters, log))
+        rows.update(_other_rows(fq, W, np, torch, dev, st, args.rows_iters, log, HE))
+    HE.close()
 
     # ------------------------------------------------------------------ CPU oracle
     cpu = None
@@ -233,7 +282,7 @@ def _row(nbytes, us_list, elems):
             "elements_per_s": round(elems / (avg * 1e-6), 1)}
 
 
-def _other_rows(fq, W, np, torch, dev, st, iters, log):
+def _other_rows(fq, W, np, torch, dev, st, iters, log, HE):
     """Each remaining hot-path operation on its own workload.  Between
     iterations, outside the events, a 1 GiB read (a max-reduction) replaces the
     256 MB Infinity Cache contents with clean lines, so inputs come from HBM
@@ -247,14 +296,13 @@ def _other_rows(fq, W, np, torch, dev, st, iters, log):
             fn()
             fn()
             us = []
+            e0, e1 = HE.new(), HE.new()
             for _ in range(iters):
                 flush.max()
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(st)
+                HE.record(e0, st)
                 fn()
-                e1.record(st)
-                e1.synchronize()
-                us.append(e0.elapsed_time(e1) * 1e3)
+                HE.record(e1, st)
+                us.append(HE.us(e0, e1))
         out[name] = _row(nbytes, us, elems)
         log(f"{name}: {out[name]['avg_us']} us, {out[name]['gbps']} GB/s")
 

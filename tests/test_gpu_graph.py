@@ -1,0 +1,74 @@
+"""GPU: the entry points are capturable into a HIP graph (torch.cuda.graph).
+Every replay, with eager work and synchronisations in between, must equal
+the eager result bit-exactly -- including the per-tensor cast, whose
+workspace is cleared by a kernel (no memset node)."""
+import numpy as np
+import torch
+
+import dequantize_amax_reduce_amd as fq
+from dequantize_amax_reduce_amd import workloads as W
+from gpu_util import host
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_all(b):
+    fq.fp8q_cast_per_group128(b["x"], b["qg"], b["sg"], "e4m3fn")
+    fq.fp8q_dequant_per_group128(b["qg"], b["sg"], b["yg"])
+    fq.fp8q_cast_per_tensor(b["x"], b["qt"], b["st"], b["ws"], "e5m2")
+    fq.fp8q_dequant_per_tensor(b["qt"], b["st"], b["yt"])
+    fq.fp8q_cast_per_channel(b["x"], b["qc"], b["sc"], "e4m3fn")
+    fq.fp8q_weight_dequant_block128(b["qw"], b["sw"], b["yw"])
+    fq.fp8q_amax(b["x"], b["amax"])
+
+
+def _outputs(b):
+    return {k: host(v).copy() for k, v in b.items() if k not in ("x", "qw", "sw", "ws")}
+
+
+def test_graph_replays_match_eager():
+    dev = torch.device("cuda:0")
+    xh, _ = W.activation_outlier_channels(rows=512, cols=7168, seed=3)
+    cw, sw = W.block_weight(M=384, N=1024, seed=4)
+    R, C = xh.shape
+    b = {
+        "x": torch.from_numpy(xh).view(torch.int16).view(torch.bfloat16).to(dev),
+        "qg": torch.empty((R, C), dtype=torch.uint8, device=dev),
+        "sg": torch.empty((R, C // 128), dtype=torch.float32, device=dev),
+        "yg": torch.empty((R, C), dtype=torch.bfloat16, device=dev),
+        "qt": torch.empty((R, C), dtype=torch.uint8, device=dev),
+        "st": torch.empty(1, dtype=torch.float32, device=dev),
+        "ws": torch.empty(4, dtype=torch.int32, device=dev),
+        "yt": torch.empty((R, C), dtype=torch.float32, device=dev),
+        "qc": torch.empty((R, C), dtype=torch.uint8, device=dev),
+        "sc": torch.empty(R, dtype=torch.float32, device=dev),
+        "qw": torch.from_numpy(cw).to(dev),
+        "sw": torch.from_numpy(sw).to(dev),
+        "yw": torch.empty(cw.shape, dtype=torch.bfloat16, device=dev),
+        "amax": torch.empty(1, dtype=torch.float32, device=dev),
+    }
+    _run_all(b)                       # eager reference (also warms up every kernel)
+    torch.cuda.synchronize()
+    want = _outputs(b)
+
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            _run_all(b)
+    torch.cuda.synchronize()
+
+    for rep in range(4):
+        for k, v in b.items():       # eager work between replays: scribble over every output
+            if k not in ("x", "qw", "sw"):
+                v.view(torch.uint8).fill_(0xA5)
+        torch.cuda.synchronize()
+        print(f"[case] graph replay {rep}", flush=True)
+        g.replay()
+        torch.cuda.synchronize()
+        got = _outputs(b)
+        for k in want:
+            assert np.array_equal(got[k].view(np.uint8), want[k].view(np.uint8)), (rep, k)
