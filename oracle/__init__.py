@@ -94,6 +94,8 @@ class OracleLib:
             "oracle_dequant_per_channel": (I, [P, I, I64, I64, P, P, I]),
             "oracle_dequant_per_group128": (I, [P, I, I64, I64, P, P, I]),
             "oracle_weight_dequant_block128": (I, [P, I, I64, I64, P, P, I]),
+            "oracle_dequant_sum": (I, [P, I, I64, I64, P, I, P, I]),
+            "oracle_dequant_sum_requant": (I, [P, I, I64, I64, P, I, P, I, P, P]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -214,6 +216,34 @@ class OracleLib:
         _check(self.L.oracle_weight_dequant_block128(_ptr(q), FORMATS[fmt], M, N, _ptr(si), _ptr(y),
                                                      DTYPES[ydtype]), "weight_dequant_block128")
         return y
+
+
+    # ---- reduce step of the compressed collectives ----------------------
+    def dequant_sum(self, q, fmt: str, scale_inv, ydtype: str, average: bool = False):
+        """q [W, n] fp8 codes, scale_inv [W] -> the chunk-ordered sum [n] in ydtype"""
+        q = np.ascontiguousarray(np.asarray(q, dtype=np.uint8))
+        W, n = q.shape
+        si = np.ascontiguousarray(np.asarray(scale_inv, dtype=np.float32).reshape(-1))
+        if si.size != W:
+            raise ValueError("dequant_sum: scale_inv must have W entries")
+        y = _out(n, ydtype)
+        _check(self.L.oracle_dequant_sum(_ptr(q), FORMATS[fmt], W, n, _ptr(si), int(average), _ptr(y),
+                                         DTYPES[ydtype]), "dequant_sum")
+        return y
+
+    def dequant_sum_requant(self, q, fmt: str, scale_inv, ydtype: str, average: bool = False):
+        """-> (summed [n] in ydtype, q_out [n], scale_inv_out [1])"""
+        q = np.ascontiguousarray(np.asarray(q, dtype=np.uint8))
+        W, n = q.shape
+        si = np.ascontiguousarray(np.asarray(scale_inv, dtype=np.float32).reshape(-1))
+        if si.size != W:
+            raise ValueError("dequant_sum_requant: scale_inv must have W entries")
+        y = _out(n, ydtype)
+        qo = np.zeros(n, dtype=np.uint8)
+        so = np.zeros(1, dtype=np.float32)
+        _check(self.L.oracle_dequant_sum_requant(_ptr(q), FORMATS[fmt], W, n, _ptr(si), int(average), _ptr(y),
+                                                 DTYPES[ydtype], _ptr(qo), _ptr(so)), "dequant_sum_requant")
+        return y, qo, so
 
 
 _default = None

@@ -351,3 +351,46 @@ int oracle_weight_dequant_block128(const uint8_t* q, int fmt, int64_t M, int64_t
                        oracle_fp8_decode(q[i * N + j], fmt) * scale_inv[(i / 128) * nb + j / 128]);
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* reduce step of the compressed collectives                                 */
+/* ------------------------------------------------------------------------ */
+
+/* value of v after rounding to the element type (binary32 holds every bf16
+ * and fp16 value exactly) */
+static float round_to(float v, int dtype) {
+    if (dtype == ORC_BF16) return oracle_f32_from_bf16(oracle_bf16_from_f32(v));
+    if (dtype == ORC_F16) return oracle_f32_from_f16(oracle_f16_from_f32(v));
+    return v;
+}
+
+/* ColossalAI fp8.py, _all_reduce_fp8 / _reduce_scatter_fp8 and the DDP hook's
+ * sum_and_allgather: summed_out = zeros(input_type); for each received chunk
+ * in order, summed_out += cast_from_fp8(chunk, its scale_inv, input_type);
+ * then summed_out.div_(world_size) for ReduceOp.AVG.  Each += is an
+ * input_type addition (binary32 sum rounded to the type), and the division
+ * is a binary32 division rounded to the type. */
+int oracle_dequant_sum(const uint8_t* q, int fmt, int64_t W, int64_t n, const float* scale_inv, int average,
+                       void* y, int ydtype) {
+    if (oracle_fpu_check()) return -9;
+    if (bad_dtype(ydtype) || bad_fmt(fmt)) return -2;
+    if (W < 1 || n < 0) return -1;
+    for (int64_t i = 0; i < n; ++i) {
+        float acc = 0.0f;
+        for (int64_t w = 0; w < W; ++w) {
+            float term = round_to(oracle_fp8_decode(q[w * n + i], fmt) * scale_inv[w], ydtype);
+            acc = round_to(acc + term, ydtype);
+        }
+        if (average) acc = round_to(acc / (float)W, ydtype);
+        store_elem(y, ydtype, i, acc);
+    }
+    return 0;
+}
+
+/* _all_reduce_fp8: the summed chunk is cast again with cast_to_fp8 (per tensor) */
+int oracle_dequant_sum_requant(const uint8_t* q, int fmt, int64_t W, int64_t n, const float* scale_inv,
+                               int average, void* y, int ydtype, uint8_t* q_out, float* scale_inv_out) {
+    int rc = oracle_dequant_sum(q, fmt, W, n, scale_inv, average, y, ydtype);
+    if (rc != 0) return rc;
+    return oracle_cast_per_tensor(y, ydtype, n, fmt, q_out, scale_inv_out);
+}

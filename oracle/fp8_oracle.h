@@ -82,6 +82,15 @@ int oracle_dequant_per_group128(const uint8_t* q, int fmt, int64_t rows, int64_t
 int oracle_weight_dequant_block128(const uint8_t* q, int fmt, int64_t M, int64_t N,
                                    const float* scale_inv, void* y, int ydtype);
 
+/* --- reduce step of the fp8-compressed all-reduce / reduce-scatter ------ */
+/* y[i] = the chunk-ordered sum over w of ydtype(fp32(q[w][i]) * scale_inv[w]),
+ * accumulated in ydtype from +0, then divided by W when `average`. */
+int oracle_dequant_sum(const uint8_t* q /*[W][n]*/, int fmt, int64_t W, int64_t n,
+                       const float* scale_inv /*[W]*/, int average, void* y, int ydtype);
+/* the sum above (written to y), then cast_to_fp8(y) per tensor into q_out / scale_inv_out[0] */
+int oracle_dequant_sum_requant(const uint8_t* q, int fmt, int64_t W, int64_t n, const float* scale_inv,
+                               int average, void* y, int ydtype, uint8_t* q_out, float* scale_inv_out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -454,4 +454,104 @@ def pin_page_worked_shapes(L):
         raise AssertionError("n % 128 != 0 must be rejected")
 
 
+# ---------------------------------------------------------------------------
+# reduce step of the compressed all-reduce / reduce-scatter
+# ---------------------------------------------------------------------------
+
+TORCH_HP = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
+def _hp_bits(t: torch.Tensor, dtype):
+    if dtype == "f32":
+        return t.numpy().view(np.uint32)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def _sum_inputs(W, n, fmt, seed):
+    """W chunks made the way the collectives make them: each a per-tensor cast
+    (with its own scale) of a tensor of a different magnitude."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = np.empty((W, n), np.uint8)
+    si = np.empty(W, np.float32)
+    fmax = float(X.fp8_value(X.FMT[fmt][3], fmt))
+    for w in range(W):
+        amax = np.float32(10.0 ** rng.uniform(-4, 3))
+        x = (rng.standard_normal(n) * amax).astype(np.float32)
+        scale = np.float32(fmax) / np.float32(np.abs(x).max())
+        q[w] = torch.from_numpy(np.clip(x * scale, -fmax, fmax)).to(TORCH_FP8[fmt]).view(torch.uint8).numpy()
+        si[w] = np.float32(1.0) / scale
+    return q, si
+
+
+def pin_dequant_sum_vs_torch(L):
+    """The pages' reduce loop evaluated by torch on the CPU: summed_out =
+    zeros(input_type); summed_out += (scale_inv * q.float()).to(input_type) per
+    chunk in order; summed_out.div_(W) for AVG (W a power of two, where torch's
+    division and a true division agree)."""
+    for fmt in FORMATS:
+        for dtype in ("bf16", "f32", "f16"):
+            for W in (1, 2, 4, 8):
+                q, si = _sum_inputs(W, 333, fmt, seed=W * 7 + len(dtype))
+                for average in (False, True):
+                    summed = torch.zeros(333, dtype=TORCH_HP[dtype])
+                    for w in range(W):
+                        term = (torch.tensor(si[w]) * torch.from_numpy(q[w]).view(TORCH_FP8[fmt]).float())
+                        summed += term.to(TORCH_HP[dtype])
+                    if average:
+                        summed.div_(W)
+                    got = L.dequant_sum(q, fmt, si, dtype, average)
+                    want = _hp_bits(summed, dtype)
+                    assert np.array_equal(np.asarray(got).view(want.dtype), want), (fmt, dtype, W, average)
+
+
+def pin_dequant_sum_exact(L):
+    """Exact rational reference on small inputs, W = 3 (not a power of two):
+    each term and each partial sum rounded to the type, then the division."""
+    rnd = {"f32": X.rn32, "bf16": X.rn_bf16, "f16": X.rn_f16}
+    for fmt in FORMATS:
+        for dtype in ("bf16", "f32", "f16"):
+            q, si = _sum_inputs(3, 40, fmt, seed=5)
+            for average in (False, True):
+                got = L.dequant_sum(q, fmt, si, dtype, average)
+                for i in range(40):
+                    acc = Fraction(0)
+                    for w in range(3):
+                        term = rnd[dtype](X.rn32(X.fp8_value(int(q[w, i]), fmt) * X.frac(si[w])))
+                        acc = rnd[dtype](X.rn32(acc + term))
+                    if average:
+                        acc = rnd[dtype](X.rn32(acc / 3))
+                    g = got[i]
+                    gv = Fraction(float(g)) if dtype == "f32" else (
+                        Fraction(float(_bf16_to_f32(g))) if dtype == "bf16" else
+                        Fraction(float(np.uint16(g).view(np.float16))))
+                    assert gv == acc, (fmt, dtype, average, i, gv, acc)
+
+
+def pin_dequant_sum_special(L):
+    """IEEE facts the loop must keep: the sum starts from +0 (zeros), so chunks
+    of -0 sum to +0; and the in-type accumulation is order dependent:
+    1 + 2^-8 + 2^-8 in chunk order is 1 in bf16 (each addition ties to even)."""
+    fmt = "e4m3fn"
+    q = np.full((3, 4), 0x80, np.uint8)                          # -0 everywhere
+    for dtype in ("bf16", "f32", "f16"):
+        y = np.asarray(L.dequant_sum(q, fmt, np.ones(3, np.float32), dtype))
+        assert np.all(y.view(np.uint32 if dtype == "f32" else np.uint16) == 0), dtype
+    one, tiny = 0x38, 0x08                                       # e4m3fn: 1.0 and 2^-6
+    q = np.array([[one], [tiny], [tiny]], np.uint8)
+    si = np.array([1.0, 0.25, 0.25], np.float32)                  # terms 1, 2^-8, 2^-8
+    y = L.dequant_sum(q, fmt, si, "bf16")
+    assert int(y[0]) == 0x3F80, hex(int(y[0]))                    # 1.0, not 1.0078125
+    y = L.dequant_sum(q[::-1].copy(), fmt, si[::-1].copy(), "bf16")
+    assert int(y[0]) == 0x3F81, hex(int(y[0]))                    # 2^-8 + 2^-8 + 1 = 1.0078125
+
+
+def pin_dequant_sum_requant_is_cast_of_sum(L):
+    for fmt in FORMATS:
+        q, si = _sum_inputs(4, 500, fmt, seed=9)
+        y, qo, so = L.dequant_sum_requant(q, fmt, si, "bf16", True)
+        wq, ws = L.cast_per_tensor(np.asarray(y), "bf16", fmt)
+        assert np.array_equal(qo, wq) and so[0] == ws[0]
+        assert np.array_equal(np.asarray(y), np.asarray(L.dequant_sum(q, fmt, si, "bf16", True)))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

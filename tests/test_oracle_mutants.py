@@ -39,6 +39,15 @@ MUTANTS = [
     ("f16_overflow_saturates", "if (code >= 0x7C00) code = 0x7C00;", "if (code >= 0x7C00) code = 0x7BFF;"),
     ("empty_channel_scale", "if (cols == 0) { scale_inv[r] = 1.0f; continue; }",
      "if (cols == 0) { scale_inv[r] = 0.0f; continue; }"),
+    ("sum_in_f32_round_once", "            acc = round_to(acc + term, ydtype);", "            acc = acc + term;"),
+    ("sum_term_unrounded", "float term = round_to(oracle_fp8_decode(q[w * n + i], fmt) * scale_inv[w], ydtype);",
+     "float term = oracle_fp8_decode(q[w * n + i], fmt) * scale_inv[w];"),
+    ("sum_starts_from_first_term", "        float acc = 0.0f;\n        for (int64_t w = 0; w < W; ++w) {",
+     "        float acc = -0.0f;\n        for (int64_t w = 0; w < W; ++w) {"),
+    ("average_by_reciprocal", "if (average) acc = round_to(acc / (float)W, ydtype);",
+     "if (average) acc = round_to(acc * (1.0f / (float)W), ydtype);"),
+    ("sum_reversed_order", "float term = round_to(oracle_fp8_decode(q[w * n + i], fmt) * scale_inv[w], ydtype);",
+     "float term = round_to(oracle_fp8_decode(q[(W - 1 - w) * n + i], fmt) * scale_inv[W - 1 - w], ydtype);"),
 ]
 
 
