@@ -326,7 +326,7 @@ def _other_rows(fq, W, np, torch, dev, st, iters, log, HE):
     amax = torch.empty(4, dtype=torch.float32, device=dev)
     qg = torch.empty(n, dtype=torch.uint8, device=dev)
     sg = torch.empty(1, dtype=torch.float32, device=dev)
-    ws = torch.empty(4, dtype=torch.int32, device=dev)
+    ws = torch.empty(fq.fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32, device=dev)
     yg = torch.empty(n, dtype=torch.float32, device=dev)
     timed("amax_bf16_268435456", n * 2 + 4, n, lambda: fq.fp8q_amax(gd, amax, stream=st))
     timed("per_tensor_cast_bf16_e5m2_268435456 (amax pass + cast pass)", 2 * n * 2 + n + 4, n,
@@ -334,6 +334,24 @@ def _other_rows(fq, W, np, torch, dev, st, iters, log, HE):
     timed("per_tensor_dequant_e5m2_f32_268435456", n + 4 + n * 4, n,
           lambda: fq.fp8q_dequant_per_tensor(qg, sg, yg, "e5m2", stream=st))
     del gd, qg, yg
+
+    # reduce step of the fp8-compressed collectives: one rank of 8 holding the
+    # 8 received e5m2 chunks of a 2^28-element bf16 gradient bucket (2^25 each)
+    log("received-chunks workload")
+    Wn, nc = 8, 1 << 25
+    ch, sc = W.received_chunks(Wn, nc, "e5m2", seed=6)
+    qd = torch.from_numpy(ch).to(dev)
+    sd = torch.from_numpy(sc).to(dev)
+    del ch
+    yd = torch.empty(nc, dtype=torch.bfloat16, device=dev)
+    qo = torch.empty(nc, dtype=torch.uint8, device=dev)
+    so = torch.empty(1, dtype=torch.float32, device=dev)
+    timed("dequant_sum_e5m2_bf16_8x33554432 (reduce-scatter reduce)", Wn * nc + 4 * Wn + 2 * nc, nc,
+          lambda: fq.fp8q_dequant_sum(qd, sd, yd, "e5m2", True, stream=st))
+    timed("dequant_sum_requant_e5m2_bf16_8x33554432 (all-reduce reduce: sum pass + cast pass)",
+          Wn * nc + 4 * Wn + 2 * nc + 2 * nc + nc + 4, nc,
+          lambda: fq.fp8q_dequant_sum_requant(qd, sd, yd, qo, so, ws, "e5m2", True, stream=st))
+    del qd, yd, qo
 
     # per-tensor and per-channel on [4096, 4096] fp32 / bf16 with row scales 10**U(-3,3)
     log("row-scaled [4096, 4096] workload")

@@ -4,7 +4,7 @@ Every step of quantize and dequantize runs in the HIP kernels of
 ``csrc/fp8q_kernels.hip`` behind the C ABI of ``include/fp8q.h``; this module
 only marshals torch tensors (device memory) and the current HIP stream into
 those calls.  There is no CPU or PyTorch fallback: importing the package fails
-if the library is not built (``python -m dequantize_amax_reduce_amd.build``).
+if the library is not built (``python dequantize_amax_reduce_amd/build.py``).
 
 Two layers:
 
@@ -40,7 +40,7 @@ _DT = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m dequantize_amax_reduce_amd.build` "
+        raise ImportError(f"{LIB_PATH} is not built; run `python dequantize_amax_reduce_amd/build.py` "
                           "(the HIP library is required; there is no fallback)")
     L = ctypes.CDLL(LIB_PATH)
     P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
@@ -56,6 +56,8 @@ def _load():
         "fp8q_dequant_per_channel": (I, [P, I, I64, I64, P, P, I, P]),
         "fp8q_dequant_per_group128": (I, [P, I, I64, I64, P, P, I, P]),
         "fp8q_weight_dequant_block128": (I, [P, I, I64, I64, P, P, I, P]),
+        "fp8q_dequant_sum": (I, [P, I, I64, I64, P, I, P, I, P]),
+        "fp8q_dequant_sum_requant": (I, [P, I, I64, I64, P, I, P, I, P, P, P, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(L, name)
@@ -68,7 +70,7 @@ lib = _load()
 ABI_FUNCTIONS = ("fp8q_abi_version", "fp8q_status_str", "fp8q_per_tensor_workspace_bytes", "fp8q_amax",
                  "fp8q_cast_per_tensor", "fp8q_cast_per_channel", "fp8q_cast_per_group128",
                  "fp8q_dequant_per_tensor", "fp8q_dequant_per_channel", "fp8q_dequant_per_group128",
-                 "fp8q_weight_dequant_block128")
+                 "fp8q_weight_dequant_block128", "fp8q_dequant_sum", "fp8q_dequant_sum_requant")
 
 
 def header_functions() -> list:
@@ -242,6 +244,36 @@ def fp8q_weight_dequant_block128(q, scale_inv, y, fmt=None, stream=None) -> None
            "fp8q_weight_dequant_block128")
 
 
+def _sum_args(q, scale_inv, y, fmt):
+    f = _fp8(q, fmt, "q")
+    if q.dim() != 2:
+        raise ValueError("q must be [W, n] (one received chunk per row)")
+    W, n = q.shape
+    if scale_inv.dtype != torch.float32 or scale_inv.numel() != W or y.numel() != n:
+        raise ValueError("scale_inv must be float32[W] and y must have n elements")
+    return f, W, n
+
+
+def fp8q_dequant_sum(q, scale_inv, y, fmt=None, average=False, stream=None) -> None:
+    f, W, n = _sum_args(q, scale_inv, y, fmt)
+    _check(lib.fp8q_dequant_sum(_dev(q, "q"), f, W, n, _dev(scale_inv, "scale_inv"), int(bool(average)),
+                                _dev(y, "y"), _hp_dtype(y, "y"), _stream(q, stream)), "fp8q_dequant_sum")
+
+
+def fp8q_dequant_sum_requant(q, scale_inv, y, q_out, scale_inv_out, workspace, fmt=None, average=False,
+                             stream=None) -> None:
+    f, W, n = _sum_args(q, scale_inv, y, fmt)
+    if q_out.numel() != n or scale_inv_out.dtype != torch.float32 or scale_inv_out.numel() < 1:
+        raise ValueError("q_out must have n elements and scale_inv_out must be float32[1]")
+    fo = _fp8(q_out, f, "q_out")
+    if workspace.numel() * workspace.element_size() < fp8q_per_tensor_workspace_bytes():
+        raise ValueError("workspace too small")
+    _check(lib.fp8q_dequant_sum_requant(_dev(q, "q"), fo, W, n, _dev(scale_inv, "scale_inv"), int(bool(average)),
+                                        _dev(y, "y"), _hp_dtype(y, "y"), _dev(q_out, "q_out"),
+                                        _dev(scale_inv_out, "scale_inv_out"), _dev(workspace, "workspace"),
+                                        _stream(q, stream)), "fp8q_dequant_sum_requant")
+
+
 # ---------------------------------------------------------------------------
 # page-level helpers (allocate outputs with torch; all compute in the kernels)
 # ---------------------------------------------------------------------------
@@ -293,6 +325,25 @@ def per_token_cast_back(q: torch.Tensor, scale_inv: torch.Tensor, ret_type=torch
     y = torch.empty(q.shape, dtype=ret_type, device=q.device)
     fp8q_dequant_per_group128(q, scale_inv, y)
     return y
+
+
+def reduce_fp8_chunks(chunks: torch.Tensor, scales: torch.Tensor, input_type: torch.dtype, average=False,
+                      requant=False, fp8_format=None):
+    """The reduce step of the fp8-compressed collectives on one rank: chunks
+    [W, n] fp8 received from W ranks with their scale_inv [W].  Returns the
+    in-type sum (reduce-scatter), or (sum, fp8 re-cast, scale_inv) with
+    requant=True (all-reduce)."""
+    W, n = chunks.shape
+    y = torch.empty(n, dtype=input_type, device=chunks.device)
+    if not requant:
+        fp8q_dequant_sum(chunks, scales, y, fp8_format, average)
+        return y
+    f = _fp8(chunks, fp8_format, "chunks")
+    qo = torch.empty(n, dtype=_FP8_DTYPE[f], device=chunks.device)
+    so = torch.empty(1, dtype=torch.float32, device=chunks.device)
+    ws = torch.empty(fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32, device=chunks.device)
+    fp8q_dequant_sum_requant(chunks, scales, y, qo, so, ws, fp8_format, average)
+    return y, qo, so
 
 
 def weight_dequant(x: torch.Tensor, s: torch.Tensor, block_size: int = 128, ret_type=torch.bfloat16):

@@ -1,6 +1,9 @@
 """Build the HIP library libfp8q.so in-tree with hipcc for gfx950.
 
-    python -m dequantize_amax_reduce_amd.build
+    python dequantize_amax_reduce_amd/build.py
+
+(run by path: importing the package loads libfp8q.so, which may be missing
+or stale before the build).
 
 Flags that matter for the numerics:
   -ffp-contract=off   no FMA contraction of the binary32 products

@@ -381,8 +381,23 @@ k_group128_wave(const void* __restrict__ x, uint8_t* __restrict__ q, float* __re
 // then the scale-and-cast pass
 // ===========================================================================
 
-__global__ void k_fill_u32(uint32_t* p, uint32_t v) {
-    if (threadIdx.x == 0) p[0] = v;
+// Amax slots: stage 2 of the global amax is an atomic max of each
+// workgroup's result into slot (workgroup % nslots); slot i is the word at
+// i * kAmaxSlotStride, one slot per 128-byte line.  Device-scope atomics
+// serialise per cache line, so slots sharing a line gain nothing.
+
+// clear the amax slots (a kernel rather than hipMemsetAsync, so the call
+// can be captured into a HIP graph)
+__global__ void k_fill_slots(uint32_t* p, int nslots, uint32_t v) {
+    if ((int)threadIdx.x < nslots) p[threadIdx.x * kAmaxSlotStride] = v;
+}
+
+// fold the slots into slot 0 (one wavefront, after the stage-2 atomics), so
+// the cast pass reads a single word
+__global__ void k_fold_slots(uint32_t* p, int nslots) {
+    uint32_t m = (int)threadIdx.x < nslots ? p[threadIdx.x * kAmaxSlotStride] : 0u;
+    m = max_lanes<64>(m);
+    if (threadIdx.x == 0) p[0] = m;
 }
 
 __global__ void k_fill_f32(float* p, int64_t n, float v) {
@@ -392,9 +407,11 @@ __global__ void k_fill_f32(float* p, int64_t n, float v) {
 
 // VEC (x 16-B aligned): chunks of K sub-steps x 256 lane vectors per
 // workgroup trip; the n % VE tail element-wise by workgroup 0.
+// Stage 2 is an atomic max of each workgroup's result into one of `nslots`
+// amax slots (workgroup b uses slot b % nslots).
 template <int DT, bool VEC, int K, bool NT>
 __global__ void __launch_bounds__(256)
-k_amax(const void* __restrict__ x, int64_t n, uint32_t* __restrict__ amax_bits) {
+k_amax(const void* __restrict__ x, int64_t n, uint32_t* __restrict__ amax_bits, int nslots) {
     __shared__ uint32_t lds[4];
     constexpr int VE = LaneVE<DT>::value;
     constexpr int ESZ = ESize<DT>::value;
@@ -423,7 +440,7 @@ k_amax(const void* __restrict__ x, int64_t n, uint32_t* __restrict__ amax_bits) 
             m = umax(m, absbits1<DT>(x, i));
     }
     m = block_max256(m, lds);
-    if (threadIdx.x == 0 && m != 0) atomicMax(amax_bits, m);
+    if (threadIdx.x == 0 && m != 0) atomicMax(amax_bits + (blockIdx.x % nslots) * kAmaxSlotStride, m);
 }
 
 // scale from the finished amax: a = amax > 0 ? amax : 1 (NaN -> 1),
@@ -744,6 +761,133 @@ k_block128_s(const uint8_t* __restrict__ q, int64_t M, int64_t N, const float* _
         const float* srow = sinv + (i / 128) * nbn;
         for (int64_t j = threadIdx.x; j < N; j += 256)
             store1<YDT>(y, i * N + j, dec1<FMT>(q[i * N + j]) * srow[j / 128]);
+    }
+}
+
+// ===========================================================================
+// reduce step of the fp8-compressed all-reduce / reduce-scatter (ColossalAI
+// fp8.py: _all_reduce_fp8, _reduce_scatter_fp8, the DDP hook's
+// sum_and_allgather)
+// ===========================================================================
+
+// v rounded to the element type, as binary32 (exact widening back)
+template <int YDT> __device__ __forceinline__ float round_to(float v) {
+    if constexpr (YDT == kBF16) return bf16_lo(pack_bf16x2(v, 0.0f));
+    else if constexpr (YDT == kF16) return (float)__builtin_bit_cast(_Float16, to_f16(v));
+    else return v;
+}
+
+// Round VE binary32 values to the element type in place (exact widening
+// back).  bf16 rounds two values per v_cvt_pk_bf16_f32; fp16 has no RNE
+// packed convert, so it goes value by value.
+template <int YDT, int VE> __device__ __forceinline__ void round_vec(float* v) {
+    if constexpr (YDT == kBF16) {
+#pragma unroll
+        for (int k = 0; k < VE; k += 2) {
+            const uint32_t w = pack_bf16x2(v[k], v[k + 1]);
+            v[k] = bf16_lo(w);
+            v[k + 1] = bf16_hi(w);
+        }
+    } else if constexpr (YDT == kF16) {
+#pragma unroll
+        for (int k = 0; k < VE; ++k) v[k] = round_to<YDT>(v[k]);
+    }
+}
+
+// One term of the sum: ydtype(fp32(q) * scale_inv), added to the running sum
+// with the type's rounding (summed_out += cast_from_fp8(...) on an ydtype
+// tensor).  The running sum starts at +0 (torch.zeros).
+template <int FMT, int YDT, int VE>
+__device__ __forceinline__ void sum_term(float* acc, const uint32_t* w, float s) {
+    float p[VE];
+#pragma unroll
+    for (int k = 0; k < VE / 4; ++k) dec4<FMT>(w[k], p + 4 * k);
+#pragma unroll
+    for (int k = 0; k < VE; ++k) p[k] = p[k] * s;
+    round_vec<YDT, VE>(p);
+#pragma unroll
+    for (int k = 0; k < VE; ++k) acc[k] = acc[k] + p[k];
+    round_vec<YDT, VE>(acc);
+}
+
+// ydtype(acc / W).  For W a power of two, a * (1/W) is the same exact value
+// as a / W (1/W is exact in binary32), so it rounds identically; any other W
+// takes the correctly rounded division.
+template <int YDT, int VE> __device__ __forceinline__ void average_vec(float* acc, float fW, bool pow2) {
+    if (pow2) {
+        const float r = 1.0f / fW;
+#pragma unroll
+        for (int k = 0; k < VE; ++k) acc[k] = acc[k] * r;
+    } else {
+#pragma unroll
+        for (int k = 0; k < VE; ++k) acc[k] = acc[k] / fW;
+    }
+    round_vec<YDT, VE>(acc);
+}
+
+// y[i] = sum over the W chunks of q (chunk w at q + w * n) in chunk order,
+// divided by W when `average`; with AMAX, max |y| is folded into the amax
+// slots (one atomic max per workgroup, slot blockIdx.x % nslots).
+// VEC: n % VE == 0, q VE-aligned, y 16-B aligned.  A thread owns KV lane
+// vectors 256 apart; chunk loads are issued four chunks at a time for all
+// of them before their terms are added.
+template <int FMT, int YDT, bool VEC, bool AMAX, bool NT, int KV>
+__global__ void __launch_bounds__(256)
+k_dequant_sum(const uint8_t* __restrict__ q, int64_t W, int64_t n, const float* __restrict__ sinv, int average,
+              void* __restrict__ y, uint32_t* __restrict__ amax_bits, int nslots) {
+    __shared__ uint32_t lds[4];
+    constexpr int VE = LaneVE<YDT>::value;
+    const float fW = (float)W;
+    const bool pow2 = (W & (W - 1)) == 0;
+    uint32_t m = 0;
+    const int64_t nvec = VEC ? n / VE : 0;
+    for (int64_t v0 = (int64_t)blockIdx.x * 256 * KV + threadIdx.x; v0 < nvec; v0 += (int64_t)gridDim.x * 256 * KV) {
+        float acc[KV][VE];
+#pragma unroll
+        for (int u = 0; u < KV; ++u)
+#pragma unroll
+            for (int k = 0; k < VE; ++k) acc[u][k] = 0.0f;
+        for (int64_t w0 = 0; w0 < W; w0 += 4) {
+            Fp8Vec<FMT, VE, NT> c[KV][4];
+#pragma unroll
+            for (int u = 0; u < KV; ++u)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (w0 + j < W && v0 + u * 256 < nvec) c[u][j].load(q + (w0 + j) * n + (v0 + u * 256) * VE);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (w0 + j < W) {
+                    const float s = sinv[w0 + j];
+#pragma unroll
+                    for (int u = 0; u < KV; ++u) sum_term<FMT, YDT, VE>(acc[u], c[u][j].w, s);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < KV; ++u) {
+            const int64_t vi = v0 + u * 256;
+            if (vi < nvec) {
+                if (average) average_vec<YDT, VE>(acc[u], fW, pow2);
+                if constexpr (AMAX) {
+#pragma unroll
+                    for (int k = 0; k < VE; ++k) m = umax(m, __float_as_uint(acc[u][k]) & 0x7FFFFFFFu);
+                }
+                store_out16<YDT, NT>(y, vi * VE, acc[u]);
+            }
+        }
+    }
+    // element-wise: the n % VE tail of the vector path, or everything
+    const int64_t nthr = (int64_t)gridDim.x * 256;
+    for (int64_t i = nvec * VE + (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += nthr) {
+        float acc = 0.0f;
+        for (int64_t w = 0; w < W; ++w) acc = round_to<YDT>(acc + round_to<YDT>(dec1<FMT>(q[w * n + i]) * sinv[w]));
+        if (average) acc = round_to<YDT>(pow2 ? acc * (1.0f / fW) : acc / fW);
+        if constexpr (AMAX) m = umax(m, __float_as_uint(acc) & 0x7FFFFFFFu);
+        store1<YDT>(y, i, acc);
+    }
+    if constexpr (AMAX) {
+        m = block_max256(m, lds);
+        if (threadIdx.x == 0 && m != 0) atomicMax(amax_bits + (blockIdx.x % nslots) * kAmaxSlotStride, m);
     }
 }
 

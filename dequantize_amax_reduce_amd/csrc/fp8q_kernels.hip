@@ -22,6 +22,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int64_t kGridCap = 1 << 20;   // grid-stride beyond this many workgroups
 constexpr int64_t kAmaxGrid = 1024;
+constexpr int64_t kSumAmaxGrid = 4096;  // the reduce step's sum pass when it also folds the amax
 
 constexpr int kGroupK = 2;        // sub-steps per group-cast chunk
 constexpr int kFlatK = 2;         // sub-steps per flat cast / dequant chunk
@@ -29,6 +30,7 @@ constexpr int kAmaxK = 2;         // sub-steps per amax chunk
 constexpr int kBlockK = 2;        // sub-steps per block-dequant chunk
 constexpr int kBlockRows = 1;     // rows per workgroup in the row-strip fallback
 constexpr int kBlockU = 2;        // lane vectors per row per thread in flight there
+constexpr int kSumKV = 2;         // lane vectors per thread in the reduce-step sum
 constexpr bool kNT = true;        // non-temporal loads/stores for streaming data
 
 inline bool al(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
@@ -95,17 +97,24 @@ template <int DT, int FMT> struct RunChannel {
     }
 };
 
-template <int DT> void run_amax(const void* x, int64_t n, uint32_t* ws, hipStream_t st) {
-    k_fill_u32<<<1, 64, 0, st>>>(ws, 0u);
+// The amax grid is capped at kAmaxGrid workgroups looping over chunks: one
+// atomic per workgroup, spread over the slots (measured on the gradient
+// workload: 83 us with 64 line-separated slots, 87 us with one word, and
+// 758 us with one word and one chunk per workgroup).
+template <int DT> void run_amax(const void* x, int64_t n, uint32_t* ws, int nslots, hipStream_t st) {
+    k_fill_slots<<<1, 64, 0, st>>>(ws, nslots, 0u);
     if (n == 0) return;
     constexpr int VE = LaneVE<DT>::value;
+    const int64_t cap = kAmaxGrid;
     if (al(x, 16)) {
         const int64_t chunks = (n / VE + kAmaxK * 256 - 1) / (kAmaxK * 256);
-        k_amax<DT, true, kAmaxK, kNT><<<(unsigned)std::min(std::max<int64_t>(chunks, 1), kAmaxGrid), kThreads, 0,
-                                        st>>>(x, n, ws);
+        k_amax<DT, true, kAmaxK, kNT><<<(unsigned)std::min(std::max<int64_t>(chunks, 1), cap), kThreads, 0,
+                                        st>>>(x, n, ws, nslots);
     } else {
-        k_amax<DT, false, kAmaxK, kNT><<<(unsigned)std::min((n + 255) / 256, kAmaxGrid), kThreads, 0, st>>>(x, n, ws);
+        k_amax<DT, false, kAmaxK, kNT><<<(unsigned)std::min((n + 255) / 256, cap), kThreads, 0, st>>>(x, n, ws,
+                                                                                                     nslots);
     }
+    if (nslots > 1) k_fold_slots<<<1, 64, 0, st>>>(ws, nslots);
 }
 
 template <int FMT, int YDT> struct RunDequantFlat {
@@ -154,16 +163,41 @@ template <int FMT, int YDT> struct RunBlock128 {
     }
 };
 
+template <int FMT, int YDT> struct RunDequantSum {
+    static void run(const uint8_t* q, int64_t W, int64_t n, const float* sinv, int average, void* y, uint32_t* ws,
+                    hipStream_t st) {
+        constexpr int VE = LaneVE<YDT>::value;
+        constexpr int KV = kSumKV;
+        const bool vec = (n % VE == 0) && al(q, VE) && al(y, 16);
+        const int64_t units = vec ? (n / VE + 256 * KV - 1) / (256 * KV) : (n + 255) / 256;
+        if (ws) {
+            k_fill_slots<<<1, 64, 0, st>>>(ws, kAmaxSlots, 0u);
+            const unsigned nb = (unsigned)std::min(std::max<int64_t>(units, 1), kSumAmaxGrid);
+            if (vec) k_dequant_sum<FMT, YDT, true, true, kNT, KV><<<nb, kThreads, 0, st>>>(q, W, n, sinv, average, y, ws, kAmaxSlots);
+            else k_dequant_sum<FMT, YDT, false, true, kNT, KV><<<nb, kThreads, 0, st>>>(q, W, n, sinv, average, y, ws, kAmaxSlots);
+            k_fold_slots<<<1, 64, 0, st>>>(ws, kAmaxSlots);
+        } else {
+            if (vec) k_dequant_sum<FMT, YDT, true, false, kNT, KV><<<grid(units), kThreads, 0, st>>>(q, W, n, sinv, average, y, ws, 1);
+            else k_dequant_sum<FMT, YDT, false, false, kNT, KV><<<grid(units), kThreads, 0, st>>>(q, W, n, sinv, average, y, ws, 1);
+        }
+    }
+};
+
 }  // namespace
+
+void launch_dequant_sum(const uint8_t* q, int fmt, int64_t W, int64_t n, const float* sinv, int average, void* y,
+                        int ydt, uint32_t* ws, hipStream_t st) {
+    dispatch_fmt_ydt<RunDequantSum>(fmt, ydt, q, W, n, sinv, average, y, ws, st);
+}
 
 void launch_fill_f32(float* p, int64_t n, float v, hipStream_t st) {
     k_fill_f32<<<grid((n + kThreads - 1) / kThreads), kThreads, 0, st>>>(p, n, v);
 }
 
-void launch_amax(const void* x, int dt, int64_t n, uint32_t* ws, hipStream_t st) {
-    if (dt == kF32) run_amax<kF32>(x, n, ws, st);
-    else if (dt == kBF16) run_amax<kBF16>(x, n, ws, st);
-    else run_amax<kF16>(x, n, ws, st);
+void launch_amax(const void* x, int dt, int64_t n, uint32_t* ws, int nslots, hipStream_t st) {
+    if (dt == kF32) run_amax<kF32>(x, n, ws, nslots, st);
+    else if (dt == kBF16) run_amax<kBF16>(x, n, ws, nslots, st);
+    else run_amax<kF16>(x, n, ws, nslots, st);
 }
 
 void launch_tensor_cast(const void* x, int dt, int64_t n, int fmt, const uint32_t* ws, uint8_t* q, float* sinv,

@@ -14,8 +14,15 @@ enum { kE4M3 = 0, kE5M2 = 1 };
 // (checked by the ABI layer): sizes > 0 unless stated, pointers valid and
 // aligned to their element size, buffers non-overlapping.
 void launch_fill_f32(float* p, int64_t n, float v, hipStream_t st);
-// clears *ws, then folds max |x| (as binary32 bits) into it; n may be 0
-void launch_amax(const void* x, int dt, int64_t n, uint32_t* ws, hipStream_t st);
+// Per-tensor amax slots: the workspace of the per-tensor cast holds
+// kAmaxSlots words, kAmaxSlotStride words (128 bytes) apart; the finished
+// amax is their max.
+constexpr int kAmaxSlots = 64;
+constexpr int kAmaxSlotStride = 32;
+// clears the nslots amax slots of ws, folds max |x| (binary32 bits) into them and
+// leaves the result in ws[0]; n may be 0
+void launch_amax(const void* x, int dt, int64_t n, uint32_t* ws, int nslots, hipStream_t st);
+// the scale-and-cast pass, with amax = ws[0]
 void launch_tensor_cast(const void* x, int dt, int64_t n, int fmt, const uint32_t* ws, uint8_t* q, float* sinv,
                         hipStream_t st);
 void launch_channel_cast(const void* x, int dt, int64_t rows, int64_t cols, int fmt, uint8_t* q, float* sinv,
@@ -28,5 +35,9 @@ void launch_dequant_rows(const uint8_t* q, int fmt, int64_t rows, int64_t cols, 
                          hipStream_t st);
 void launch_block128(const uint8_t* q, int fmt, int64_t M, int64_t N, const float* sinv, void* y, int ydt,
                      hipStream_t st);
+// y = chunk-ordered in-type sum of the W dequantized chunks of q (W x n), / W if average;
+// with ws != nullptr, the kAmaxSlots slots of ws are cleared first and max |y| ends in ws[0]
+void launch_dequant_sum(const uint8_t* q, int fmt, int64_t W, int64_t n, const float* sinv, int average, void* y,
+                        int ydt, uint32_t* ws, hipStream_t st);
 
 }  // namespace fp8q

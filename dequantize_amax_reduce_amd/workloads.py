@@ -110,3 +110,14 @@ def fp8_codes_finite(shape, fmt: str, seed: int):
         bad = {0x7C, 0x7D, 0x7E, 0x7F, 0xFC, 0xFD, 0xFE, 0xFF}
     table = np.array([c for c in range(256) if c not in bad], dtype=np.uint8)
     return table[rng.integers(0, table.size, size=shape)]
+
+
+def received_chunks(W: int, n: int, fmt: str = "e5m2", seed: int = 6, lo: float = -6.0, hi: float = -2.0):
+    """What one rank holds at the reduce step of an fp8-compressed collective:
+    W chunks of n fp8 codes (uniform over the finite codes) received from W
+    ranks, each with its own per-tensor scale_inv = 10**U(lo, hi).
+    Returns (uint8 codes [W, n], float32 scale_inv [W])."""
+    rng = _rng(seed)
+    codes = fp8_codes_finite((W, n), fmt, seed=seed + 1000)
+    s = (10.0 ** rng.uniform(lo, hi, size=W)).astype(np.float32)
+    return codes, s

@@ -68,7 +68,10 @@ int fp8q_abi_version(void);
 /* static, human-readable name of a status code (never NULL) */
 const char* fp8q_status_str(int status);
 
-/* bytes of device workspace fp8q_cast_per_tensor needs (4, rounded up to 16) */
+/* bytes of device workspace fp8q_cast_per_tensor and fp8q_dequant_sum_requant
+ * need (8192): 64 binary32 amax slots, one per 128-byte line; the stage-1
+ * workgroups fold their maxima into slot (workgroup % 64), so the atomics do
+ * not serialise on one cache line */
 size_t fp8q_per_tensor_workspace_bytes(void);
 
 /*
@@ -153,6 +156,37 @@ fp8q_status_t fp8q_dequant_per_group128(const uint8_t* q, int fmt, int64_t rows,
  */
 fp8q_status_t fp8q_weight_dequant_block128(const uint8_t* q, int fmt, int64_t M, int64_t N,
                                            const float* scale_inv, void* y, int ydtype, void* stream);
+
+/*
+ * Reduce step of an fp8-compressed reduce-scatter / all-reduce, on one rank
+ * (ColossalAI fp8.py: _reduce_scatter_fp8's cast_op, _all_reduce_fp8 and the
+ * DDP hook's sum_and_allgather).  The rank has received W fp8 chunks of n
+ * elements, each cast per tensor by a different rank with its own scale_inv:
+ *   q: [W][n] codes (chunk w at q + w * n); scale_inv: [W] floats;
+ *   y[i] = sum over w in chunk order of ydtype(fp32(q[w][i]) * scale_inv[w]),
+ *          accumulated in ydtype starting from +0 (summed_out = zeros, then
+ *          summed_out += cast_from_fp8(...) per chunk: every term and every
+ *          partial sum is rounded to ydtype);
+ *   average != 0 (ReduceOp.AVG, and the DDP hook): y = ydtype(y / W), a
+ *          correctly rounded binary32 division.
+ * ydtype is the original tensor's type (input_type on the page).  W >= 1.
+ * n == 0 is a no-op.
+ */
+fp8q_status_t fp8q_dequant_sum(const uint8_t* q, int fmt, int64_t W, int64_t n, const float* scale_inv,
+                               int average, void* y, int ydtype, void* stream);
+
+/*
+ * fp8q_dequant_sum followed by cast_to_fp8 of the sum, per tensor
+ * (_all_reduce_fp8: summed_out_fp8, scale = cast_to_fp8(summed_out)): y
+ * receives the sum (it is also the intermediate), q_out[n] its fp8 codes in the
+ * same format and scale_inv_out[0] = 1 / scale.  The amax of the sum is folded
+ * into `workspace` (at least fp8q_per_tensor_workspace_bytes(), 4-byte
+ * aligned, caller-owned) during the sum pass, so y is read once more, by the
+ * cast pass.  n == 0 writes scale_inv_out[0] = 1.0 (the empty-tensor branch).
+ */
+fp8q_status_t fp8q_dequant_sum_requant(const uint8_t* q, int fmt, int64_t W, int64_t n, const float* scale_inv,
+                                       int average, void* y, int ydtype, uint8_t* q_out, float* scale_inv_out,
+                                       void* workspace, void* stream);
 
 #ifdef __cplusplus
 }

@@ -40,7 +40,7 @@ def test_graph_replays_match_eager():
         "yg": torch.empty((R, C), dtype=torch.bfloat16, device=dev),
         "qt": torch.empty((R, C), dtype=torch.uint8, device=dev),
         "st": torch.empty(1, dtype=torch.float32, device=dev),
-        "ws": torch.empty(4, dtype=torch.int32, device=dev),
+        "ws": torch.empty(fq.fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32, device=dev),
         "yt": torch.empty((R, C), dtype=torch.float32, device=dev),
         "qc": torch.empty((R, C), dtype=torch.uint8, device=dev),
         "sc": torch.empty(R, dtype=torch.float32, device=dev),

@@ -25,7 +25,7 @@ def _tensor_cast(xh, dtype, fmt, x_offset=0):
     x = flat[x_offset:]
     q = torch.empty(n, dtype=torch.uint8, device="cuda:0")
     s = torch.empty(1, dtype=torch.float32, device="cuda:0")
-    ws = torch.empty(4, dtype=torch.int32, device="cuda:0")
+    ws = torch.empty(fq.fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32, device="cuda:0")
     print(f"[case] per-tensor cast {dtype} {fmt} n={n} x_off={x_offset}", flush=True)
     fq.fp8q_cast_per_tensor(x, q, s, ws, fmt)
     torch.cuda.synchronize()
@@ -193,7 +193,7 @@ def test_gradient_payload_full_size():
     fq.fp8q_amax(xd, a)
     q = torch.empty(x.size, dtype=torch.uint8, device="cuda:0")
     s = torch.empty(1, dtype=torch.float32, device="cuda:0")
-    ws = torch.empty(4, dtype=torch.int32, device="cuda:0")
+    ws = torch.empty(fq.fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32, device="cuda:0")
     print("[case] gradient payload cast", flush=True)
     fq.fp8q_cast_per_tensor(xd, q, s, ws, "e5m2")
     y = torch.empty(x.size, dtype=torch.float32, device="cuda:0")
@@ -216,7 +216,7 @@ def test_empty_tensors():
         x = torch.empty(0, dtype=torch.float32, device="cuda:0")
         q = torch.empty(0, dtype=torch.uint8, device="cuda:0")
         s = torch.full((1,), -7.0, dtype=torch.float32, device="cuda:0")
-        ws = torch.empty(4, dtype=torch.int32, device="cuda:0")
+        ws = torch.empty(fq.fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32, device="cuda:0")
         fq.fp8q_cast_per_tensor(x, q, s, ws, fmt)
         torch.cuda.synchronize()
         assert host(s)[0] == 1.0                           # cast_to_fp8's empty branch
