@@ -96,6 +96,9 @@ class OracleLib:
             "oracle_weight_dequant_block128": (I, [P, I, I64, I64, P, P, I]),
             "oracle_dequant_sum": (I, [P, I, I64, I64, P, I, P, I]),
             "oracle_dequant_sum_requant": (I, [P, I, I64, I64, P, I, P, I, P, P]),
+            "oracle_amax_guarded": (F, [P, I, I64]),
+            "oracle_cast_with_amax": (I, [P, I, I64, I, F, P, P]),
+            "oracle_dequant_div_scale": (I, [P, I, I64, F, P, I]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -244,6 +247,28 @@ class OracleLib:
         _check(self.L.oracle_dequant_sum_requant(_ptr(q), FORMATS[fmt], W, n, _ptr(si), int(average), _ptr(y),
                                                  DTYPES[ydtype], _ptr(qo), _ptr(so)), "dequant_sum_requant")
         return y, qo, so
+
+
+    # ---- FSDP parameter hook: cross-rank global amax -----------------------
+    def amax_guarded(self, x, dtype: str) -> np.float32:
+        x = _in(x, dtype)
+        return np.float32(self.L.oracle_amax_guarded(_ptr(x), DTYPES[dtype], x.size))
+
+    def cast_with_amax(self, x, dtype: str, fmt: str, amax):
+        """-> (q with x's shape, scale float32[1])"""
+        x = _in(x, dtype)
+        q = np.zeros(x.shape, dtype=np.uint8)
+        sc = np.zeros(1, dtype=np.float32)
+        _check(self.L.oracle_cast_with_amax(_ptr(x), DTYPES[dtype], x.size, FORMATS[fmt], float(np.float32(amax)),
+                                            _ptr(q), _ptr(sc)), "cast_with_amax")
+        return q, sc
+
+    def dequant_div_scale(self, q, fmt: str, scale, ydtype: str):
+        q = np.ascontiguousarray(np.asarray(q, dtype=np.uint8))
+        y = _out(q.shape, ydtype)
+        _check(self.L.oracle_dequant_div_scale(_ptr(q), FORMATS[fmt], q.size, float(np.float32(scale)), _ptr(y),
+                                               DTYPES[ydtype]), "dequant_div_scale")
+        return y
 
 
 _default = None

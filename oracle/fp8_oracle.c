@@ -394,3 +394,37 @@ int oracle_dequant_sum_requant(const uint8_t* q, int fmt, int64_t W, int64_t n, 
     if (rc != 0) return rc;
     return oracle_cast_per_tensor(y, ydtype, n, fmt, q_out, scale_inv_out);
 }
+
+/* ------------------------------------------------------------------------ */
+/* FSDP parameter hook: a global scale from a cross-rank amax                */
+/* ------------------------------------------------------------------------ */
+
+/* ColossalAI fp8.py, fp8_compress_fsdp_params_comm_hook: per_tensor_max =
+ * inp.abs().max().float(), then torch.where(per_tensor_max > 0, ., 1.0) on
+ * each rank before dist.all_reduce(per_tensor_max, op=MAX). */
+float oracle_amax_guarded(const void* x, int dtype, int64_t n) {
+    float amax = oracle_amax(x, dtype, n);
+    return (amax > 0.0f) ? amax : 1.0f;
+}
+
+/* the same hook after the all-reduce: scale = fp8_max / per_tensor_max;
+ * fp8 = (scale * inp.float()).to(fp8_type) */
+int oracle_cast_with_amax(const void* x, int dtype, int64_t n, int fmt, float amax, uint8_t* q, float* scale_out) {
+    if (oracle_fpu_check()) return -9;
+    if (bad_dtype(dtype) || bad_fmt(fmt)) return -2;
+    if (n < 0) return -1;
+    float scale = oracle_fp8_max(fmt) / amax;
+    oracle_scale_and_cast(x, dtype, n, scale, fmt, q);
+    scale_out[0] = scale;
+    return 0;
+}
+
+/* the hook's dequant after the all-gather: (fp8_out.float() / scale).to(out.dtype),
+ * a binary32 division (not a product with 1/scale) */
+int oracle_dequant_div_scale(const uint8_t* q, int fmt, int64_t n, float scale, void* y, int ydtype) {
+    if (oracle_fpu_check()) return -9;
+    if (bad_dtype(ydtype) || bad_fmt(fmt)) return -2;
+    if (n < 0) return -1;
+    for (int64_t i = 0; i < n; ++i) store_elem(y, ydtype, i, oracle_fp8_decode(q[i], fmt) / scale);
+    return 0;
+}

@@ -91,6 +91,14 @@ int oracle_dequant_sum(const uint8_t* q /*[W][n]*/, int fmt, int64_t W, int64_t 
 int oracle_dequant_sum_requant(const uint8_t* q, int fmt, int64_t W, int64_t n, const float* scale_inv,
                                int average, void* y, int ydtype, uint8_t* q_out, float* scale_inv_out);
 
+/* --- cross-rank global amax (FSDP parameter hook) ----------------------- */
+/* where(max|x| > 0, max|x|, 1): the local value each rank contributes to the MAX all-reduce */
+float oracle_amax_guarded(const void* x, int dtype, int64_t n);
+/* scale = fp8_max / amax (amax: the reduced, guarded value); q = enc(fp32(x) * scale); *scale_out = scale */
+int oracle_cast_with_amax(const void* x, int dtype, int64_t n, int fmt, float amax, uint8_t* q, float* scale_out);
+/* y = ydtype(fp32(q) / scale): the dequant by division */
+int oracle_dequant_div_scale(const uint8_t* q, int fmt, int64_t n, float scale, void* y, int ydtype);
+
 #ifdef __cplusplus
 }
 #endif

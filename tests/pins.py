@@ -554,4 +554,51 @@ def pin_dequant_sum_requant_is_cast_of_sum(L):
         assert np.array_equal(np.asarray(y), np.asarray(L.dequant_sum(q, fmt, si, "bf16", True)))
 
 
+# ---------------------------------------------------------------------------
+# FSDP parameter hook: cross-rank global amax, cast with it, dequant by division
+# ---------------------------------------------------------------------------
+
+def pin_fsdp_hook_vs_torch(L):
+    """The hook's expressions evaluated by torch on the CPU for two simulated
+    ranks: per_tensor_max = where(abs().max().float() > 0, ., 1) per rank, MAX
+    over the ranks, scale = fp8_max / max (written as a true division, R8),
+    (scale * inp.float()).to(fp8), then (fp8.float() / scale).to(out.dtype)."""
+    rng = np.random.Generator(np.random.PCG64(41))
+    for fmt in FORMATS:
+        fmax = float(X.fp8_value(X.FMT[fmt][3], fmt))
+        for dtype in ("bf16", "f32", "f16"):
+            shards = [(rng.standard_normal(257) * 10.0 ** rng.uniform(-3, 2)).astype(np.float32) for _ in range(2)]
+            shards.append(np.zeros(100, np.float32))                  # a rank holding zeros contributes 1
+            hs = [torch.from_numpy(s_).to(TORCH_HP[dtype]) for s_ in shards]
+            host = [_hp_bits(h, dtype) if dtype != "f32" else h.numpy() for h in hs]
+            locs = [torch.where(h.abs().max().float() > 0, h.abs().max().float(), torch.tensor(1.0)) for h in hs]
+            for h_, t in zip(host, locs):
+                assert np.float32(L.amax_guarded(h_, dtype)) == np.float32(t.item()), (fmt, dtype)
+            gmax = torch.stack(locs).max()
+            scale = torch.div(torch.tensor(fmax, dtype=torch.float32), gmax)
+            for h, h_ in zip(hs, host):
+                want_q = (scale * h.float()).to(TORCH_FP8[fmt]).view(torch.uint8).numpy()
+                q, sc = L.cast_with_amax(h_, dtype, fmt, gmax.item())
+                assert np.float32(sc[0]) == np.float32(scale.item()), (fmt, dtype)
+                assert np.array_equal(q, want_q), (fmt, dtype)
+                for ydt in ("bf16", "f32", "f16"):
+                    want_y = (torch.from_numpy(q).view(TORCH_FP8[fmt]).float() / scale).to(TORCH_HP[ydt])
+                    got = np.asarray(L.dequant_div_scale(q, fmt, sc[0], ydt))
+                    assert np.array_equal(got.view(np.uint8), _hp_bits(want_y, ydt).view(np.uint8)), (fmt, dtype, ydt)
+
+
+def pin_dequant_div_scale_exact(L):
+    """Division, not a product with 1/scale: exact rationals on every code."""
+    for fmt in FORMATS:
+        maxc = X.FMT[fmt][3]
+        codes = np.array([c for c in range(256) if (c & 0x7F) <= maxc], dtype=np.uint8)
+        for sc in (np.float32(3.0), np.float32(0.1), np.float32(448.0 / 2.7)):
+            for ydt, rnd in (("f32", X.rn32), ("bf16", X.rn_bf16)):
+                y = L.dequant_div_scale(codes, fmt, sc, ydt)
+                for c, g in zip(codes, y):
+                    want = rnd(X.rn32(X.fp8_value(int(c), fmt) / X.frac(sc)))
+                    gv = Fraction(float(g)) if ydt == "f32" else Fraction(float(_bf16_to_f32(g)))
+                    assert gv == want, (fmt, hex(int(c)), sc, ydt)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -46,6 +46,9 @@ MUTANTS = [
      "        float acc = -0.0f;\n        for (int64_t w = 0; w < W; ++w) {"),
     ("average_by_reciprocal", "if (average) acc = round_to(acc / (float)W, ydtype);",
      "if (average) acc = round_to(acc * (1.0f / (float)W), ydtype);"),
+    ("fsdp_dequant_by_reciprocal", "store_elem(y, ydtype, i, oracle_fp8_decode(q[i], fmt) / scale);",
+     "store_elem(y, ydtype, i, oracle_fp8_decode(q[i], fmt) * (1.0f / scale));"),
+    ("fsdp_guard_dropped", "    return (amax > 0.0f) ? amax : 1.0f;\n}", "    return amax;\n}"),
     ("sum_reversed_order", "float term = round_to(oracle_fp8_decode(q[w * n + i], fmt) * scale_inv[w], ydtype);",
      "float term = round_to(oracle_fp8_decode(q[(W - 1 - w) * n + i], fmt) * scale_inv[W - 1 - w], ydtype);"),
 ]
