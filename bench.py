@@ -333,6 +333,15 @@ def _other_rows(fq, W, np, torch, dev, st, iters, log, HE):
           lambda: fq.fp8q_cast_per_tensor(gd, qg, sg, ws, "e5m2", stream=st))
     timed("per_tensor_dequant_e5m2_f32_268435456", n + 4 + n * 4, n,
           lambda: fq.fp8q_dequant_per_tensor(qg, sg, yg, "e5m2", stream=st))
+    # FSDP parameter hook's parts on the same shard: cast with a given (all-reduced)
+    # amax, dequant by division by the scale
+    yb = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    fq.fp8q_amax_guarded(gd, amax, stream=st)
+    timed("cast_with_amax_bf16_e5m2_268435456 (FSDP hook, one pass)", n * 2 + n + 8, n,
+          lambda: fq.fp8q_cast_with_amax(gd, amax, qg, sg, "e5m2", stream=st))
+    timed("dequant_div_scale_e5m2_bf16_268435456 (FSDP hook)", n + 4 + n * 2, n,
+          lambda: fq.fp8q_dequant_div_scale(qg, sg, yb, "e5m2", stream=st))
+    del yb
     del gd, qg, yg
 
     # reduce step of the fp8-compressed collectives: one rank of 8 holding the

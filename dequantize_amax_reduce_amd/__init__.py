@@ -56,6 +56,9 @@ def _load():
         "fp8q_dequant_per_channel": (I, [P, I, I64, I64, P, P, I, P]),
         "fp8q_dequant_per_group128": (I, [P, I, I64, I64, P, P, I, P]),
         "fp8q_weight_dequant_block128": (I, [P, I, I64, I64, P, P, I, P]),
+        "fp8q_amax_guarded": (I, [P, I, I64, P, P]),
+        "fp8q_cast_with_amax": (I, [P, I, I64, I, P, P, P, P]),
+        "fp8q_dequant_div_scale": (I, [P, I, I64, P, P, I, P]),
         "fp8q_dequant_sum": (I, [P, I, I64, I64, P, I, P, I, P]),
         "fp8q_dequant_sum_requant": (I, [P, I, I64, I64, P, I, P, I, P, P, P, P]),
     }
@@ -70,7 +73,8 @@ lib = _load()
 ABI_FUNCTIONS = ("fp8q_abi_version", "fp8q_status_str", "fp8q_per_tensor_workspace_bytes", "fp8q_amax",
                  "fp8q_cast_per_tensor", "fp8q_cast_per_channel", "fp8q_cast_per_group128",
                  "fp8q_dequant_per_tensor", "fp8q_dequant_per_channel", "fp8q_dequant_per_group128",
-                 "fp8q_weight_dequant_block128", "fp8q_dequant_sum", "fp8q_dequant_sum_requant")
+                 "fp8q_weight_dequant_block128", "fp8q_dequant_sum", "fp8q_dequant_sum_requant",
+                 "fp8q_amax_guarded", "fp8q_cast_with_amax", "fp8q_dequant_div_scale")
 
 
 def header_functions() -> list:
@@ -242,6 +246,29 @@ def fp8q_weight_dequant_block128(q, scale_inv, y, fmt=None, stream=None) -> None
     _check(lib.fp8q_weight_dequant_block128(_dev(q, "q"), f, M, N, _dev(scale_inv, "scale_inv"), _dev(y, "y"),
                                             _hp_dtype(y, "y"), _stream(q, stream)),
            "fp8q_weight_dequant_block128")
+
+
+def fp8q_amax_guarded(x: torch.Tensor, amax: torch.Tensor, stream=None) -> None:
+    if amax.dtype != torch.float32 or amax.numel() < 1:
+        raise TypeError("amax must be a float32 tensor with at least one element")
+    _check(lib.fp8q_amax_guarded(_dev(x, "x"), _hp_dtype(x, "x"), x.numel(), _dev(amax, "amax"),
+                                 _stream(x, stream)), "fp8q_amax_guarded")
+
+
+def fp8q_cast_with_amax(x, amax, q, scale_out, fmt="e5m2", stream=None) -> None:
+    f = _fp8(q, fmt, "q")
+    if q.numel() != x.numel() or amax.dtype != torch.float32 or scale_out.dtype != torch.float32:
+        raise ValueError("fp8q_cast_with_amax: q must match x; amax and scale_out must be float32")
+    _check(lib.fp8q_cast_with_amax(_dev(x, "x"), _hp_dtype(x, "x"), x.numel(), f, _dev(amax, "amax"), _dev(q, "q"),
+                                   _dev(scale_out, "scale_out"), _stream(x, stream)), "fp8q_cast_with_amax")
+
+
+def fp8q_dequant_div_scale(q, scale, y, fmt=None, stream=None) -> None:
+    f = _fp8(q, fmt, "q")
+    if y.numel() != q.numel() or scale.dtype != torch.float32:
+        raise ValueError("fp8q_dequant_div_scale: y must match q and scale must be float32[1]")
+    _check(lib.fp8q_dequant_div_scale(_dev(q, "q"), f, q.numel(), _dev(scale, "scale"), _dev(y, "y"),
+                                      _hp_dtype(y, "y"), _stream(q, stream)), "fp8q_dequant_div_scale")
 
 
 def _sum_args(q, scale_inv, y, fmt):

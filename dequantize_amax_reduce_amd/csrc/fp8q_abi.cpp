@@ -101,6 +101,39 @@ fp8q_status_t fp8q_amax(const void* x, int xdtype, int64_t n, float* amax, void*
     return launched();
 }
 
+fp8q_status_t fp8q_amax_guarded(const void* x, int xdtype, int64_t n, float* amax, void* stream) {
+    fp8q_status_t st = fp8q_amax(x, xdtype, n, amax, stream);
+    if (st != FP8Q_OK) return st;
+    fp8q::launch_guard_amax((uint32_t*)amax, S(stream));
+    return launched();
+}
+
+fp8q_status_t fp8q_cast_with_amax(const void* x, int xdtype, int64_t n, int fmt, const float* amax, uint8_t* q,
+                                  float* scale_out, void* stream) {
+    if (n < 0) return FP8Q_EINVAL;
+    int64_t nn;
+    fp8q_status_t st = check_2d(x, xdtype, 1, n, fmt, q, scale_out, 1, &nn);
+    if (st != FP8Q_OK) return st;
+    if (!amax) return FP8Q_EINVAL;
+    if (!aligned(amax, 4)) return FP8Q_EALIGN;
+    const Buf b[4] = {{x, n * esize(xdtype)}, {q, n}, {scale_out, 4}, {amax, 4}};
+    if (any_overlap(b, 4)) return FP8Q_EINVAL;
+    // n == 0 still launches one workgroup: the scale is written, no element is
+    fp8q::launch_cast_given_amax(x, xdtype, n, fmt, amax, q, scale_out, S(stream));
+    return launched();
+}
+
+fp8q_status_t fp8q_dequant_div_scale(const uint8_t* q, int fmt, int64_t n, const float* scale, void* y, int ydtype,
+                                     void* stream) {
+    if (n < 0) return FP8Q_EINVAL;
+    int64_t nn;
+    fp8q_status_t st = check_2d(y, ydtype, 1, n, fmt, q, scale, n > 0 ? 1 : 0, &nn);
+    if (st != FP8Q_OK) return st;
+    if (n == 0) return FP8Q_OK;
+    fp8q::launch_dequant_flat(3, q, fmt, n, scale, y, ydtype, S(stream));
+    return launched();
+}
+
 fp8q_status_t fp8q_cast_per_tensor(const void* x, int xdtype, int64_t n, int fmt, uint8_t* q, float* scale_inv,
                                    void* workspace, void* stream) {
     if (n < 0) return FP8Q_EINVAL;

@@ -392,6 +392,14 @@ __global__ void k_fill_slots(uint32_t* p, int nslots, uint32_t v) {
     if ((int)threadIdx.x < nslots) p[threadIdx.x * kAmaxSlotStride] = v;
 }
 
+// where(amax > 0, amax, 1) in place (a NaN amax also becomes 1), on one word
+__global__ void k_guard_amax(uint32_t* p) {
+    if (threadIdx.x == 0) {
+        const float v = __uint_as_float(p[0]);
+        p[0] = __float_as_uint(v > 0.0f ? v : 1.0f);
+    }
+}
+
 // fold the slots into slot 0 (one wavefront, after the stage-2 atomics), so
 // the cast pass reads a single word
 __global__ void k_fold_slots(uint32_t* p, int nslots) {
@@ -505,6 +513,20 @@ k_tensor_cast(const void* __restrict__ x, int64_t n, const uint32_t* __restrict_
     else tensor_cast_body<DT, FMT, VEC, K, NT, false>(x, n, scale, q);
 }
 
+// Cast with a caller-supplied amax (ColossalAI fp8.py,
+// fp8_compress_fsdp_params_comm_hook: the guarded local amax reduced with MAX
+// across ranks): scale = fp8_max / amax, scale_out[0] = scale.  The given
+// amax need not bound this tensor's values, so the saturating path is always
+// taken.
+template <int DT, int FMT, bool VEC, int K, bool NT>
+__global__ void __launch_bounds__(256)
+k_cast_given_amax(const void* __restrict__ x, int64_t n, const float* __restrict__ amax, uint8_t* __restrict__ q,
+                  float* __restrict__ scale_out) {
+    const float scale = Fp8Fmt<FMT>::max / amax[0];
+    if (blockIdx.x == 0 && threadIdx.x == 0) scale_out[0] = scale;
+    tensor_cast_body<DT, FMT, VEC, K, NT, true>(x, n, scale, q);
+}
+
 // ===========================================================================
 // per-channel cast (ColossalAI fp8.py, cast_to_fp8 with per_channel_scale):
 // one 256-thread workgroup per row
@@ -587,9 +609,19 @@ k_channel_2pass(const void* __restrict__ x, int64_t rows, int64_t cols, uint8_t*
 // ===========================================================================
 
 // MODE 0: per-tensor (s = scale_inv[0]); MODE 2: per-128-group over a
-// contiguous [rows, cols % 128 == 0] tensor (s = scale_inv[e / 128]).
+// contiguous [rows, cols % 128 == 0] tensor (s = scale_inv[e / 128]);
+// MODE 3: per-tensor division by a scale (y = fp32(q) / scale[0], the FSDP
+// parameter hook's dequant; a correctly rounded division, not a product with
+// 1 / scale).
 // VEC: q aligned to VE bytes and y 16-B aligned; chunks of K sub-steps x 256
 // lane vectors; the n % VE tail element-wise by workgroup 0.
+// one element of the flat dequant (the element-wise path and the tail)
+template <int FMT, int MODE> __device__ __forceinline__ float flat_elem(uint8_t c, const float* sinv, int64_t i) {
+    if constexpr (MODE == 3) return dec1<FMT>(c) / sinv[0];
+    else if constexpr (MODE == 2) return dec1<FMT>(c) * sinv[i >> 7];
+    else return dec1<FMT>(c) * sinv[0];
+}
+
 template <int FMT, int YDT, int MODE, bool VEC, int K, bool NT>
 __global__ void __launch_bounds__(256)
 k_dequant_flat(const uint8_t* __restrict__ q, int64_t n, const float* __restrict__ sinv, void* __restrict__ y) {
@@ -597,7 +629,7 @@ k_dequant_flat(const uint8_t* __restrict__ q, int64_t n, const float* __restrict
     if constexpr (VEC) {
         const int64_t nvec = n / VE;
         const int64_t nchunks = (nvec + K * 256 - 1) / (K * 256);
-        const float s0 = (MODE == 0) ? sinv[0] : 0.0f;
+        const float s0 = (MODE != 2) ? sinv[0] : 0.0f;
         for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
             Fp8Vec<FMT, VE, NT> w[K];
 #pragma unroll
@@ -609,18 +641,23 @@ k_dequant_flat(const uint8_t* __restrict__ q, int64_t n, const float* __restrict
             for (int k = 0; k < K; ++k) {
                 const int64_t vi = (c * K + k) * 256 + threadIdx.x;
                 if (vi < nvec) {
-                    const float s = (MODE == 0) ? s0 : sinv[(vi * VE) >> 7];
                     float p[VE];
-                    w[k].decode_scaled(s, p);
+                    if constexpr (MODE == 3) {
+                        w[k].decode_scaled(1.0f, p);
+#pragma unroll
+                        for (int e = 0; e < VE; ++e) p[e] = p[e] / s0;
+                    } else {
+                        w[k].decode_scaled((MODE == 0) ? s0 : sinv[(vi * VE) >> 7], p);
+                    }
                     store_out16<YDT, NT>(y, vi * VE, p);
                 }
             }
         }
         const int64_t i = nvec * VE + threadIdx.x;
-        if (blockIdx.x == 0 && i < n) store1<YDT>(y, i, dec1<FMT>(q[i]) * ((MODE == 0) ? sinv[0] : sinv[i >> 7]));
+        if (blockIdx.x == 0 && i < n) store1<YDT>(y, i, flat_elem<FMT, MODE>(q[i], sinv, i));
     } else {
         for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-            store1<YDT>(y, i, dec1<FMT>(q[i]) * ((MODE == 0) ? sinv[0] : sinv[i >> 7]));
+            store1<YDT>(y, i, flat_elem<FMT, MODE>(q[i], sinv, i));
     }
 }
 

@@ -83,6 +83,19 @@ template <int DT, int FMT> struct RunTensorCast {
     }
 };
 
+template <int DT, int FMT> struct RunCastGivenAmax {
+    static void run(const void* x, int64_t n, const float* amax, uint8_t* q, float* scale_out, hipStream_t st) {
+        constexpr int VE = LaneVE<DT>::value;
+        if (al(x, 16) && al(q, VE)) {
+            const int64_t chunks = (n / VE + kFlatK * 256 - 1) / (kFlatK * 256);
+            k_cast_given_amax<DT, FMT, true, kFlatK, kNT><<<grid(chunks), kThreads, 0, st>>>(x, n, amax, q, scale_out);
+        } else {
+            k_cast_given_amax<DT, FMT, false, kFlatK, kNT><<<grid((n + 255) / 256), kThreads, 0, st>>>(x, n, amax, q,
+                                                                                                       scale_out);
+        }
+    }
+};
+
 template <int DT, int FMT> struct RunChannel {
     static void run(const void* x, int64_t rows, int64_t cols, uint8_t* q, float* sinv, hipStream_t st) {
         constexpr int VE = LaneVE<DT>::value;
@@ -125,6 +138,9 @@ template <int FMT, int YDT> struct RunDequantFlat {
         if (mode == 0) {
             if (vec) k_dequant_flat<FMT, YDT, 0, true, kFlatK, kNT><<<nb, kThreads, 0, st>>>(q, n, sinv, y);
             else k_dequant_flat<FMT, YDT, 0, false, kFlatK, kNT><<<nb, kThreads, 0, st>>>(q, n, sinv, y);
+        } else if (mode == 3) {
+            if (vec) k_dequant_flat<FMT, YDT, 3, true, kFlatK, kNT><<<nb, kThreads, 0, st>>>(q, n, sinv, y);
+            else k_dequant_flat<FMT, YDT, 3, false, kFlatK, kNT><<<nb, kThreads, 0, st>>>(q, n, sinv, y);
         } else {
             if (vec) k_dequant_flat<FMT, YDT, 2, true, kFlatK, kNT><<<nb, kThreads, 0, st>>>(q, n, sinv, y);
             else k_dequant_flat<FMT, YDT, 2, false, kFlatK, kNT><<<nb, kThreads, 0, st>>>(q, n, sinv, y);
@@ -203,6 +219,13 @@ void launch_amax(const void* x, int dt, int64_t n, uint32_t* ws, int nslots, hip
 void launch_tensor_cast(const void* x, int dt, int64_t n, int fmt, const uint32_t* ws, uint8_t* q, float* sinv,
                         hipStream_t st) {
     dispatch_dt_fmt<RunTensorCast>(dt, fmt, x, n, ws, q, sinv, st);
+}
+
+void launch_guard_amax(uint32_t* ws, hipStream_t st) { k_guard_amax<<<1, 64, 0, st>>>(ws); }
+
+void launch_cast_given_amax(const void* x, int dt, int64_t n, int fmt, const float* amax, uint8_t* q,
+                            float* scale_out, hipStream_t st) {
+    dispatch_dt_fmt<RunCastGivenAmax>(dt, fmt, x, n, amax, q, scale_out, st);
 }
 
 void launch_channel_cast(const void* x, int dt, int64_t rows, int64_t cols, int fmt, uint8_t* q, float* sinv,

@@ -22,13 +22,19 @@ constexpr int kAmaxSlotStride = 32;
 // clears the nslots amax slots of ws, folds max |x| (binary32 bits) into them and
 // leaves the result in ws[0]; n may be 0
 void launch_amax(const void* x, int dt, int64_t n, uint32_t* ws, int nslots, hipStream_t st);
+// where(amax > 0, amax, 1) applied to ws[0]
+void launch_guard_amax(uint32_t* ws, hipStream_t st);
+// cast with scale = fp8_max / amax[0] (caller-supplied amax); scale_out[0] = scale
+void launch_cast_given_amax(const void* x, int dt, int64_t n, int fmt, const float* amax, uint8_t* q,
+                            float* scale_out, hipStream_t st);
 // the scale-and-cast pass, with amax = ws[0]
 void launch_tensor_cast(const void* x, int dt, int64_t n, int fmt, const uint32_t* ws, uint8_t* q, float* sinv,
                         hipStream_t st);
 void launch_channel_cast(const void* x, int dt, int64_t rows, int64_t cols, int fmt, uint8_t* q, float* sinv,
                          hipStream_t st);
 void launch_group128_cast(const void* x, int dt, int64_t groups, int fmt, uint8_t* q, float* sinv, hipStream_t st);
-// mode 0: per-tensor scale; mode 2: per-128-group scale over a flat [rows * cols] with cols % 128 == 0
+// mode 0: per-tensor scale; mode 2: per-128-group scale over a flat [rows * cols] with cols % 128 == 0;
+// mode 3: per-tensor division by sinv[0] (a scale, not its inverse)
 void launch_dequant_flat(int mode, const uint8_t* q, int fmt, int64_t n, const float* sinv, void* y, int ydt,
                          hipStream_t st);
 void launch_dequant_rows(const uint8_t* q, int fmt, int64_t rows, int64_t cols, const float* sinv, void* y, int ydt,

@@ -158,6 +158,29 @@ fp8q_status_t fp8q_weight_dequant_block128(const uint8_t* q, int fmt, int64_t M,
                                            const float* scale_inv, void* y, int ydtype, void* stream);
 
 /*
+ * Cross-rank global scale, one rank's parts (ColossalAI fp8.py,
+ * fp8_compress_fsdp_params_comm_hook).  The hook computes each rank's
+ * per_tensor_max = where(max |x| > 0, max |x|, 1), all-reduces it with MAX,
+ * casts with scale = fp8_max / per_tensor_max, all-gathers the fp8 payload
+ * and dequantizes it with fp8.float() / scale.  The all-reduce and the
+ * all-gather are the caller's (e.g. torch.distributed over RCCL).
+ *
+ * fp8q_amax_guarded: amax[0] = where(max |x| > 0, max |x|, 1) (a NaN amax or
+ *   n == 0 also gives 1); same arguments and stages as fp8q_amax.
+ * fp8q_cast_with_amax: scale = fp8_max / amax[0] (a correctly rounded
+ *   binary32 division; amax is a device float, typically the all-reduced
+ *   value), q[i] = fp8(fp32(x[i]) * scale) with the saturating rule (the given
+ *   amax need not bound x), scale_out[0] = scale.  n == 0 writes only the scale.
+ * fp8q_dequant_div_scale: y[i] = ydtype(fp32(q[i]) / scale[0]) -- a division by
+ *   the scale, which rounds differently from a product with 1 / scale.
+ */
+fp8q_status_t fp8q_amax_guarded(const void* x, int xdtype, int64_t n, float* amax, void* stream);
+fp8q_status_t fp8q_cast_with_amax(const void* x, int xdtype, int64_t n, int fmt, const float* amax, uint8_t* q,
+                                  float* scale_out, void* stream);
+fp8q_status_t fp8q_dequant_div_scale(const uint8_t* q, int fmt, int64_t n, const float* scale, void* y, int ydtype,
+                                     void* stream);
+
+/*
  * Reduce step of an fp8-compressed reduce-scatter / all-reduce, on one rank
  * (ColossalAI fp8.py: _reduce_scatter_fp8's cast_op, _all_reduce_fp8 and the
  * DDP hook's sum_and_allgather).  The rank has received W fp8 chunks of n

@@ -90,6 +90,27 @@ def test_dequant_errors():
     assert b(None, E4, 0, 16, None, None, BF16, None) == fq.OK
 
 
+def test_fsdp_hook_errors():
+    g = L.fp8q_amax_guarded
+    assert g(P(A), BF16, 10, None, None) == fq.EINVAL
+    assert g(P(A), 7, 10, P(A + 4096), None) == fq.EDTYPE
+    assert g(P(A), F32, 10, P(A + 4), None) == fq.EINVAL                                   # overlap
+    c = L.fp8q_cast_with_amax
+    assert c(P(A), BF16, -1, E5, P(A + 9000), P(A + 4096), P(A + 8192), None) == fq.EINVAL
+    assert c(P(A), BF16, 16, E5, None, P(A + 4096), P(A + 8192), None) == fq.EINVAL         # no amax
+    assert c(P(A), BF16, 16, E5, P(A + 9001), P(A + 4096), P(A + 8192), None) == fq.EALIGN
+    assert c(P(A), BF16, 16, E5, P(A + 8), P(A + 4096), P(A + 8192), None) == fq.EINVAL     # amax in x
+    assert c(P(A), BF16, 16, E5, P(A + 8192), P(A + 4096), P(A + 8192), None) == fq.EINVAL  # amax = scale
+    assert c(P(A), BF16, 16, 3, P(A + 9000), P(A + 4096), P(A + 8192), None) == fq.EDTYPE
+    assert c(P(A), BF16, 16, E5, P(A + 9000), P(A + 4096), None, None) == fq.EINVAL         # no scale out
+    d = L.fp8q_dequant_div_scale
+    assert d(P(A), E5, 16, None, P(A + 4096), BF16, None) == fq.EINVAL
+    assert d(P(A), E5, 16, P(A + 8192), P(A + 4097), BF16, None) == fq.EALIGN
+    assert d(P(A), E5, 16, P(A + 8192), P(A + 8), F32, None) == fq.EINVAL                  # q/y overlap
+    assert d(P(A), E5, -3, P(A + 8192), P(A + 4096), F32, None) == fq.EINVAL
+    assert d(None, E5, 0, None, None, F32, None) == fq.OK
+
+
 def test_python_binding_rejects_host_tensors():
     import torch
     x = torch.zeros((2, 128), dtype=torch.bfloat16)
