@@ -28,6 +28,7 @@ LIB = os.path.join(_HERE, "libfp8_oracle.so")
 
 DTYPES = {"f32": 0, "bf16": 1, "f16": 2}
 FORMATS = {"e4m3fn": 0, "e5m2": 1}
+FORMAT_NAMES = {v: k for k, v in FORMATS.items()}
 
 
 def build(force: bool = True, src: str = SRC, out: str = LIB) -> str:
@@ -99,6 +100,8 @@ class OracleLib:
             "oracle_amax_guarded": (F, [P, I, I64]),
             "oracle_cast_with_amax": (I, [P, I, I64, I, F, P, P]),
             "oracle_dequant_div_scale": (I, [P, I, I64, F, P, I]),
+            "oracle_cast_to_fp8_pipeline": (I, [P, I, I64, P, P, P]),
+            "oracle_cast_from_fp8_pipeline": (I, [P, I, I64, F, P, I]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -268,6 +271,23 @@ class OracleLib:
         y = _out(q.shape, ydtype)
         _check(self.L.oracle_dequant_div_scale(_ptr(q), FORMATS[fmt], q.size, float(np.float32(scale)), _ptr(y),
                                                DTYPES[ydtype]), "dequant_div_scale")
+        return y
+
+    def cast_to_fp8_pipeline(self, x, dtype: str):
+        """-> (q with x's shape, scale_inv float32[1], fmt name)"""
+        x = _in(x, dtype)
+        q = np.zeros(x.shape, dtype=np.uint8)
+        si = np.zeros(1, dtype=np.float32)
+        f = np.zeros(1, dtype=np.int32)
+        _check(self.L.oracle_cast_to_fp8_pipeline(_ptr(x), DTYPES[dtype], x.size, _ptr(q), _ptr(si), _ptr(f)),
+               "cast_to_fp8_pipeline")
+        return q, si, FORMAT_NAMES[int(f[0])]
+
+    def cast_from_fp8_pipeline(self, q, fmt: str, scale_inv, ydtype: str):
+        q = np.ascontiguousarray(np.asarray(q, dtype=np.uint8))
+        y = _out(q.shape, ydtype)
+        _check(self.L.oracle_cast_from_fp8_pipeline(_ptr(q), FORMATS[fmt], q.size, float(np.float32(scale_inv)),
+                                                    _ptr(y), DTYPES[ydtype]), "cast_from_fp8_pipeline")
         return y
 
 

@@ -428,3 +428,46 @@ int oracle_dequant_div_scale(const uint8_t* q, int fmt, int64_t n, float scale, 
     for (int64_t i = 0; i < n; ++i) store_elem(y, ydtype, i, oracle_fp8_decode(q[i], fmt) / scale);
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* pipeline p2p cast with the format chosen from the data                    */
+/* ------------------------------------------------------------------------ */
+
+/* ColossalAI fp8.py, cast_to_fp8_pipeline: (min, max) = aminmax(x);
+ * amax = maximum(|min|, |max|) (NaN if any element is NaN); e5m2 when
+ * amax > 448 (the e4m3fn maximum), else e4m3fn; scale = 1 when amax == 0,
+ * else that format's maximum / amax (binary32 division; a NaN amax fails both
+ * comparisons, so e4m3fn with a NaN scale); q = enc(fp32(x) * scale);
+ * fp8_scale = 1 / scale.  An empty tensor is taken to have amax 0. */
+int oracle_cast_to_fp8_pipeline(const void* x, int dtype, int64_t n, uint8_t* q, float* scale_inv, int* fmt_out) {
+    if (oracle_fpu_check()) return -9;
+    if (bad_dtype(dtype)) return -2;
+    if (n < 0) return -1;
+    float lo = 0.0f, hi = 0.0f;
+    int seen = 0, saw_nan = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        float v = load_elem(x, dtype, i);
+        if (isnan(v)) { saw_nan = 1; continue; }
+        if (!seen || v < lo) lo = v;
+        if (!seen || v > hi) hi = v;
+        seen = 1;
+    }
+    float amax = saw_nan ? NAN : (fabsf(lo) > fabsf(hi) ? fabsf(lo) : fabsf(hi));
+    int fmt = (amax > oracle_fp8_max(ORC_E4M3FN)) ? ORC_E5M2 : ORC_E4M3FN;
+    float scale = (amax == 0.0f) ? 1.0f : oracle_fp8_max(fmt) / amax;
+    oracle_scale_and_cast(x, dtype, n, scale, fmt, q);
+    *scale_inv = 1.0f / scale;
+    *fmt_out = fmt;
+    return 0;
+}
+
+/* cast_from_fp8_pipeline: hidden_states.view(fp8).to(dtype) * fp8_scale -- the
+ * code converted to the output type (exact for every fp8 value), times the
+ * binary32 scale in binary32, rounded to the output type */
+int oracle_cast_from_fp8_pipeline(const uint8_t* q, int fmt, int64_t n, float scale_inv, void* y, int ydtype) {
+    if (oracle_fpu_check()) return -9;
+    if (bad_dtype(ydtype) || bad_fmt(fmt)) return -2;
+    if (n < 0) return -1;
+    for (int64_t i = 0; i < n; ++i) store_elem(y, ydtype, i, round_to(oracle_fp8_decode(q[i], fmt), ydtype) * scale_inv);
+    return 0;
+}

@@ -99,6 +99,14 @@ int oracle_cast_with_amax(const void* x, int dtype, int64_t n, int fmt, float am
 /* y = ydtype(fp32(q) / scale): the dequant by division */
 int oracle_dequant_div_scale(const uint8_t* q, int fmt, int64_t n, float scale, void* y, int ydtype);
 
+/* --- pipeline p2p cast: the format chosen from the data ----------------- */
+/* amax = max(|min|, |max|); *fmt_out = e5m2 if amax > 448 else e4m3fn;
+ * scale = 1 if amax == 0 else fp8_max(fmt) / amax; q = enc(fp32(x) * scale);
+ * *scale_inv = 1 / scale */
+int oracle_cast_to_fp8_pipeline(const void* x, int dtype, int64_t n, uint8_t* q, float* scale_inv, int* fmt_out);
+/* y = ydtype(ydtype(fp32(q)) * scale_inv) */
+int oracle_cast_from_fp8_pipeline(const uint8_t* q, int fmt, int64_t n, float scale_inv, void* y, int ydtype);
+
 #ifdef __cplusplus
 }
 #endif

@@ -601,4 +601,98 @@ def pin_dequant_div_scale_exact(L):
                     assert gv == want, (fmt, hex(int(c)), sc, ydt)
 
 
+# ---------------------------------------------------------------------------
+# pipeline p2p cast: the format chosen from the data
+# ---------------------------------------------------------------------------
+
+def pin_pipeline_vs_torch(L):
+    """cast_to_fp8_pipeline / cast_from_fp8_pipeline evaluated by torch on the
+    CPU: aminmax, maximum of the absolute values, the 448 threshold, the zero
+    test, scale = finfo.max / amax (a true division, R8), (x.float() * scale)
+    .to(fp8), fp8_scale = scale.reciprocal(); back: q.to(dtype) * fp8_scale."""
+    rng = np.random.Generator(np.random.PCG64(43))
+    for dtype in ("bf16", "f32", "f16"):
+        cases = [rng.standard_normal(300) * 10.0 ** e for e in (-3, 0, 2, 2.7, 3.5)]
+        cases += [np.zeros(64), np.array([448.0, -3.0]), np.array([-1.0, 2.0, -449.0 if dtype != "bf16" else -450.0])]
+        for xv in cases:
+            h = torch.from_numpy(np.asarray(xv, np.float32)).to(TORCH_HP[dtype])
+            lo, hi = h.aminmax()
+            amax = torch.maximum(lo.abs(), hi.abs())
+            fmt = "e5m2" if amax > torch.finfo(torch.float8_e4m3fn).max else "e4m3fn"
+            fmax = torch.finfo(TORCH_FP8[fmt]).max
+            scale = torch.tensor(1.0) if amax == 0.0 else torch.div(torch.tensor(fmax, dtype=torch.float32), amax.float())
+            want_q = (h.float() * scale).to(TORCH_FP8[fmt]).view(torch.uint8).numpy()
+            want_si = scale.float().reciprocal()
+            host = _hp_bits(h, dtype) if dtype != "f32" else h.numpy()
+            q, si, gfmt = L.cast_to_fp8_pipeline(host, dtype)
+            assert gfmt == fmt, (dtype, gfmt, fmt)
+            assert np.array_equal(q, want_q), (dtype, fmt)
+            assert np.float32(si[0]).view(np.uint32) == np.float32(want_si.item()).view(np.uint32), (dtype, fmt)
+            for ydt in ("bf16", "f32", "f16"):
+                want_y = torch.from_numpy(q).view(TORCH_FP8[fmt]).to(TORCH_HP[ydt]) * want_si
+                got = np.asarray(L.cast_from_fp8_pipeline(q, fmt, si[0], ydt))
+                assert np.array_equal(got.view(np.uint8), _hp_bits(want_y, ydt).view(np.uint8)), (dtype, fmt, ydt)
+
+
+def pin_pipeline_format_rule(L):
+    """The threshold and the degenerate amax values, from their definitions:
+    amax = 448 keeps e4m3fn with scale 1; the next value up in each type
+    switches to e5m2; the element at amax always lands on the format's largest
+    code; zero gives scale 1; NaN keeps e4m3fn with a NaN scale (NaN codes);
+    inf gives e5m2 with scale 0 (finite -> signed zero, inf -> NaN); an empty
+    tensor is amax 0."""
+    nxt = {"f32": np.float32(np.nextafter(np.float32(448), np.float32(np.inf))),
+           "bf16": np.float32(450.0), "f16": np.float32(448.25)}
+    for dtype in ("f32", "bf16", "f16"):
+        enc = (lambda v: (np.asarray(v, np.float32).view(np.uint32) >> 16).astype(np.uint16)) if dtype == "bf16" else (  # exact values only
+            (lambda v: np.asarray(v, np.float32).astype(np.float16).view(np.uint16)) if dtype == "f16" else
+            (lambda v: np.asarray(v, np.float32)))
+        q, si, f = L.cast_to_fp8_pipeline(enc(np.array([448.0, -1.0, 0.5], np.float32)), dtype)
+        assert f == "e4m3fn" and si[0] == 1.0 and list(q) == [0x7E, 0xB8, 0x30], (dtype, q, si, f)
+        q, si, f = L.cast_to_fp8_pipeline(enc(np.array([0.25, -nxt[dtype]], np.float32)), dtype)
+        want_scale = X.rn32(Fraction(57344) / X.frac(nxt[dtype]))
+        assert f == "e5m2" and q[1] == 0xFB, (dtype, q, f)
+        assert X.frac(si[0]) == X.rn32(1 / want_scale), dtype
+        q, si, f = L.cast_to_fp8_pipeline(enc(np.zeros(5, np.float32)), dtype)
+        assert f == "e4m3fn" and si[0] == 1.0 and not q.any(), dtype
+        q, si, f = L.cast_to_fp8_pipeline(enc(np.array([1.0, np.nan, -2.0], np.float32)), dtype)
+        assert f == "e4m3fn" and np.isnan(si[0]) and all((int(c) & 0x7F) == 0x7F for c in q), (dtype, q)
+        q, si, f = L.cast_to_fp8_pipeline(enc(np.array([1.0, -np.inf, -2.0], np.float32)), dtype)
+        assert f == "e5m2" and si[0] == np.inf and q[0] == 0x00 and q[2] == 0x80, (dtype, q, si)
+        assert (int(q[1]) & 0x7F) > 0x7C, (dtype, q)              # -inf * 0 = NaN
+        q, si, f = L.cast_to_fp8_pipeline(enc(np.zeros(0, np.float32)), dtype)
+        assert f == "e4m3fn" and si[0] == 1.0 and q.size == 0
+    rng = np.random.Generator(np.random.PCG64(44))
+    for _ in range(20):
+        x = (rng.standard_normal(257) * 10.0 ** rng.uniform(-5, 5)).astype(np.float32)
+        q, si, f = L.cast_to_fp8_pipeline(x, "f32")
+        i = int(np.argmax(np.abs(x)))
+        assert (int(q[i]) & 0x7F) == X.FMT[f][3], (f, hex(int(q[i])))
+        assert f == ("e5m2" if np.abs(x).max() > 448 else "e4m3fn")
+    # amax so small that fmax / amax overflows: the scale is inf, zero -> NaN,
+    # nonzero -> the largest code (saturation, R2)
+    q, si, f = L.cast_to_fp8_pipeline(np.array([1e-40, 0.0, -1e-40], np.float32), "f32")
+    assert f == "e4m3fn" and si[0] == 0.0 and q[0] == 0x7E and (int(q[1]) & 0x7F) == 0x7F and q[2] == 0xFE, (q, si)
+
+
+def pin_pipeline_dequant_exact(L):
+    """Back from either format, every code, exact rationals: the code's value
+    (exact in every output type) times scale_inv, rounded to binary32, then to
+    the output type; equal to the per-tensor dequant."""
+    for fmt in FORMATS:
+        maxc = X.FMT[fmt][3]
+        codes = np.array([c for c in range(256) if (c & 0x7F) <= maxc], dtype=np.uint8)
+        for si in (np.float32(1.0), np.float32(0.1), np.float32(1.0 / 448.0 * 3.3), np.float32(2.0 ** -20)):
+            for ydt, rnd in (("f32", X.rn32), ("bf16", X.rn_bf16), ("f16", X.rn_f16)):
+                y = L.cast_from_fp8_pipeline(codes, fmt, si, ydt)
+                assert np.array_equal(np.asarray(y).view(np.uint8),
+                                      np.asarray(L.dequant_per_tensor(codes, fmt, np.array([si]), ydt)).view(np.uint8))
+                if ydt == "f16":
+                    continue
+                for c, g in zip(codes, y):
+                    want = rnd(X.rn32(X.fp8_value(int(c), fmt) * X.frac(si)))
+                    gv = Fraction(float(g)) if ydt == "f32" else Fraction(float(_bf16_to_f32(g)))
+                    assert gv == want, (fmt, hex(int(c)), si, ydt)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -51,6 +51,18 @@ MUTANTS = [
     ("fsdp_guard_dropped", "    return (amax > 0.0f) ? amax : 1.0f;\n}", "    return amax;\n}"),
     ("sum_reversed_order", "float term = round_to(oracle_fp8_decode(q[w * n + i], fmt) * scale_inv[w], ydtype);",
      "float term = round_to(oracle_fp8_decode(q[(W - 1 - w) * n + i], fmt) * scale_inv[W - 1 - w], ydtype);"),
+    ("pipeline_threshold_inclusive", "int fmt = (amax > oracle_fp8_max(ORC_E4M3FN)) ? ORC_E5M2 : ORC_E4M3FN;",
+     "int fmt = (amax >= oracle_fp8_max(ORC_E4M3FN)) ? ORC_E5M2 : ORC_E4M3FN;"),
+    ("pipeline_guard_positive", "float scale = (amax == 0.0f) ? 1.0f : oracle_fp8_max(fmt) / amax;",
+     "float scale = (amax > 0.0f) ? oracle_fp8_max(fmt) / amax : 1.0f;"),
+    ("pipeline_scale_e4m3_max", "float scale = (amax == 0.0f) ? 1.0f : oracle_fp8_max(fmt) / amax;",
+     "float scale = (amax == 0.0f) ? 1.0f : oracle_fp8_max(ORC_E4M3FN) / amax;"),
+    ("pipeline_amax_from_max_only", "float amax = saw_nan ? NAN : (fabsf(lo) > fabsf(hi) ? fabsf(lo) : fabsf(hi));",
+     "float amax = saw_nan ? NAN : fabsf(hi);"),
+    ("pipeline_scale_inv_is_amax_over_max", "    *scale_inv = 1.0f / scale;\n    *fmt_out = fmt;",
+     "    *scale_inv = amax / oracle_fp8_max(fmt);\n    *fmt_out = fmt;"),
+    ("pipeline_dequant_scale_rounded", "round_to(oracle_fp8_decode(q[i], fmt), ydtype) * scale_inv);",
+     "round_to(oracle_fp8_decode(q[i], fmt), ydtype) * round_to(scale_inv, ydtype));"),
 ]
 
 
