@@ -190,12 +190,13 @@ def main():
     copy_us = HE.us(e0, e1) / 10
     copy_gbps = 2 * cp_n / (copy_us * 1e-6) / 1e9
     del a, b
-    del sets, x0
+    del sets
     torch.cuda.empty_cache()
 
     # ------------------------------------------------------------------ other rows
     if not args.no_rows:
-        rows.update(_other_rows(fq, W, np, torch, dev, st, args.rows_iters, log, HE))
+        rows.update(_other_rows(fq, W, np, torch, dev, st, args.rows_iters, log, HE, x0))
+    del x0
     HE.close()
 
     # ------------------------------------------------------------------ CPU oracle
@@ -282,7 +283,7 @@ def _row(nbytes, us_list, elems):
             "elements_per_s": round(elems / (avg * 1e-6), 1)}
 
 
-def _other_rows(fq, W, np, torch, dev, st, iters, log, HE):
+def _other_rows(fq, W, np, torch, dev, st, iters, log, HE, act):
     """Each remaining hot-path operation on its own workload.  Between
     iterations, outside the events, a 1 GiB read (a max-reduction) replaces the
     256 MB Infinity Cache contents with clean lines, so inputs come from HBM
@@ -305,6 +306,20 @@ def _other_rows(fq, W, np, torch, dev, st, iters, log, HE):
                 us.append(HE.us(e0, e1))
         out[name] = _row(nbytes, us, elems)
         log(f"{name}: {out[name]['avg_us']} us, {out[name]['gbps']} GB/s")
+
+    # pipeline p2p cast of the activation (bf16 [16384, 7168]) with the format
+    # chosen on the device, and back to bf16
+    na = act.numel()
+    qa = torch.empty(na, dtype=torch.uint8, device=dev)
+    sa = torch.empty(1, dtype=torch.float32, device=dev)
+    wa = torch.empty(1, dtype=torch.int32, device=dev)
+    wsa = torch.empty(fq.fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32, device=dev)
+    ya = torch.empty(na, dtype=torch.bfloat16, device=dev)
+    timed("pipeline_cast_bf16_16384x7168 (amax pass + cast pass, format chosen on the device)",
+          2 * na * 2 + na + 4 + 4, na, lambda: fq.fp8q_cast_to_fp8_pipeline(act, qa, sa, wa, wsa, stream=st))
+    timed("pipeline_dequant_bf16_16384x7168 (format read on the device)", na + 4 + 4 + na * 2, na,
+          lambda: fq.fp8q_cast_from_fp8_pipeline(qa, wa, sa, ya, stream=st))
+    del qa, sa, wa, wsa, ya
 
     # 128x128 block weight dequant: e4m3fn [18432, 7168] + float32 [144, 56] -> bf16
     log("block weight workload")

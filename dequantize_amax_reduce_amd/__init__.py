@@ -59,6 +59,8 @@ def _load():
         "fp8q_amax_guarded": (I, [P, I, I64, P, P]),
         "fp8q_cast_with_amax": (I, [P, I, I64, I, P, P, P, P]),
         "fp8q_dequant_div_scale": (I, [P, I, I64, P, P, I, P]),
+        "fp8q_cast_to_fp8_pipeline": (I, [P, I, I64, P, P, P, P, P]),
+        "fp8q_cast_from_fp8_pipeline": (I, [P, P, I64, P, P, I, P]),
         "fp8q_dequant_sum": (I, [P, I, I64, I64, P, I, P, I, P]),
         "fp8q_dequant_sum_requant": (I, [P, I, I64, I64, P, I, P, I, P, P, P, P]),
     }
@@ -74,7 +76,8 @@ ABI_FUNCTIONS = ("fp8q_abi_version", "fp8q_status_str", "fp8q_per_tensor_workspa
                  "fp8q_cast_per_tensor", "fp8q_cast_per_channel", "fp8q_cast_per_group128",
                  "fp8q_dequant_per_tensor", "fp8q_dequant_per_channel", "fp8q_dequant_per_group128",
                  "fp8q_weight_dequant_block128", "fp8q_dequant_sum", "fp8q_dequant_sum_requant",
-                 "fp8q_amax_guarded", "fp8q_cast_with_amax", "fp8q_dequant_div_scale")
+                 "fp8q_amax_guarded", "fp8q_cast_with_amax", "fp8q_dequant_div_scale",
+                 "fp8q_cast_to_fp8_pipeline", "fp8q_cast_from_fp8_pipeline")
 
 
 def header_functions() -> list:
@@ -271,6 +274,36 @@ def fp8q_dequant_div_scale(q, scale, y, fmt=None, stream=None) -> None:
                                       _hp_dtype(y, "y"), _stream(q, stream)), "fp8q_dequant_div_scale")
 
 
+def _word(t: torch.Tensor, name: str) -> int:
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.int32 or t.numel() < 1:
+        raise TypeError(f"{name} must be an int32 tensor with at least one element")
+    return _dev(t, name)
+
+
+def fp8q_cast_to_fp8_pipeline(x, q, scale_inv, fmt_out, workspace, stream=None) -> None:
+    """q: uint8 codes (the format is only known on the device); fmt_out:
+    int32[1] on the device, 0 = e4m3fn, 1 = e5m2."""
+    if q.dtype != torch.uint8 or q.numel() != x.numel():
+        raise ValueError("fp8q_cast_to_fp8_pipeline: q must be uint8 codes matching x")
+    if scale_inv.dtype != torch.float32 or scale_inv.numel() < 1:
+        raise ValueError("fp8q_cast_to_fp8_pipeline: scale_inv must be float32[1]")
+    if workspace.numel() * workspace.element_size() < fp8q_per_tensor_workspace_bytes():
+        raise ValueError("fp8q_cast_to_fp8_pipeline: workspace too small")
+    _check(lib.fp8q_cast_to_fp8_pipeline(_dev(x, "x"), _hp_dtype(x, "x"), x.numel(), _dev(q, "q"),
+                                         _dev(scale_inv, "scale_inv"), _word(fmt_out, "fmt_out"),
+                                         _dev(workspace, "workspace"), _stream(x, stream)),
+           "fp8q_cast_to_fp8_pipeline")
+
+
+def fp8q_cast_from_fp8_pipeline(q, fmt, scale_inv, y, stream=None) -> None:
+    if q.dtype != torch.uint8 or y.numel() != q.numel() or scale_inv.dtype != torch.float32:
+        raise ValueError("fp8q_cast_from_fp8_pipeline: q must be uint8 codes, y must match q and "
+                         "scale_inv must be float32[1]")
+    _check(lib.fp8q_cast_from_fp8_pipeline(_dev(q, "q"), _word(fmt, "fmt"), q.numel(), _dev(scale_inv, "scale_inv"),
+                                           _dev(y, "y"), _hp_dtype(y, "y"), _stream(q, stream)),
+           "fp8q_cast_from_fp8_pipeline")
+
+
 def _sum_args(q, scale_inv, y, fmt):
     f = _fp8(q, fmt, "q")
     if q.dim() != 2:
@@ -371,6 +404,41 @@ def reduce_fp8_chunks(chunks: torch.Tensor, scales: torch.Tensor, input_type: to
     ws = torch.empty(fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32, device=chunks.device)
     fp8q_dequant_sum_requant(chunks, scales, y, qo, so, ws, fp8_format, average)
     return y, qo, so
+
+
+def cast_to_fp8_pipeline(inp) -> None:
+    """ColossalAI fp8.py cast_to_fp8_pipeline, in place on the dict: the
+    "hidden_states" tensor becomes uint8 fp8 codes, "fp8_scale" its scale_inv
+    (float32[1]), "fp8_format" the device int32 word naming the format the
+    kernel chose (the page encodes it in the view dtype, which needs amax on
+    the host), and "dtype" the original element type.  None and bare tensors
+    are left alone, as on the page."""
+    if inp is None or isinstance(inp, torch.Tensor):
+        return
+    x = inp["hidden_states"]
+    dev = x.device
+    q = torch.empty(x.shape, dtype=torch.uint8, device=dev)
+    sinv = torch.empty(1, dtype=torch.float32, device=dev)
+    word = torch.empty(1, dtype=torch.int32, device=dev)
+    ws = torch.empty(fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32, device=dev)
+    fp8q_cast_to_fp8_pipeline(x, q, sinv, word, ws)
+    inp["hidden_states"] = q
+    inp["fp8_scale"] = sinv
+    inp["fp8_format"] = word
+    inp["dtype"] = x.dtype
+
+
+def cast_from_fp8_pipeline(inp, del_metadata=True) -> None:
+    """ColossalAI fp8.py cast_from_fp8_pipeline: hidden_states back to the
+    recorded dtype, the format taken from the device word."""
+    if inp is None or isinstance(inp, torch.Tensor):
+        return
+    q = inp["hidden_states"]
+    y = torch.empty(q.shape, dtype=inp["dtype"], device=q.device)
+    fp8q_cast_from_fp8_pipeline(q, inp["fp8_format"], inp["fp8_scale"], y)
+    inp["hidden_states"] = y
+    if del_metadata:
+        del inp["fp8_scale"], inp["fp8_format"], inp["dtype"]
 
 
 def weight_dequant(x: torch.Tensor, s: torch.Tensor, block_size: int = 128, ret_type=torch.bfloat16):

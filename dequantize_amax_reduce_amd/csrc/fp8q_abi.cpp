@@ -134,6 +134,39 @@ fp8q_status_t fp8q_dequant_div_scale(const uint8_t* q, int fmt, int64_t n, const
     return launched();
 }
 
+fp8q_status_t fp8q_cast_to_fp8_pipeline(const void* x, int xdtype, int64_t n, uint8_t* q, float* scale_inv,
+                                        int32_t* fmt_out, void* workspace, void* stream) {
+    if (n < 0) return FP8Q_EINVAL;
+    int64_t nn;
+    fp8q_status_t st = check_2d(x, xdtype, 1, n, FP8Q_E4M3FN, q, scale_inv, 1, &nn);
+    if (st != FP8Q_OK) return st;
+    if (!workspace || !fmt_out) return FP8Q_EINVAL;
+    if (!aligned(workspace, 4) || !aligned(fmt_out, 4)) return FP8Q_EALIGN;
+    const int64_t wsb = (int64_t)fp8q_per_tensor_workspace_bytes();
+    const Buf b[5] = {{x, n * esize(xdtype)}, {q, n}, {scale_inv, 4}, {workspace, wsb}, {fmt_out, 4}};
+    if (any_overlap(b, 5)) return FP8Q_EINVAL;
+    // n == 0: the amax pass only clears the slots (amax 0); the cast launches
+    // one workgroup that writes scale_inv and the format word
+    fp8q::launch_amax(x, xdtype, n, (uint32_t*)workspace, fp8q::kAmaxSlots, S(stream));
+    fp8q::launch_pipeline_cast(x, xdtype, n, (const uint32_t*)workspace, q, scale_inv, fmt_out, S(stream));
+    return launched();
+}
+
+fp8q_status_t fp8q_cast_from_fp8_pipeline(const uint8_t* q, const int32_t* fmt, int64_t n, const float* scale_inv,
+                                          void* y, int ydtype, void* stream) {
+    if (n < 0) return FP8Q_EINVAL;
+    int64_t nn;
+    fp8q_status_t st = check_2d(y, ydtype, 1, n, FP8Q_E4M3FN, q, scale_inv, n > 0 ? 1 : 0, &nn);
+    if (st != FP8Q_OK) return st;
+    if (n == 0) return FP8Q_OK;
+    if (!fmt) return FP8Q_EINVAL;
+    if (!aligned(fmt, 4)) return FP8Q_EALIGN;
+    const Buf b[3] = {{y, n * esize(ydtype)}, {q, n}, {fmt, 4}};
+    if (any_overlap(b, 3)) return FP8Q_EINVAL;
+    fp8q::launch_dequant_pipeline(q, n, scale_inv, fmt, y, ydtype, S(stream));
+    return launched();
+}
+
 fp8q_status_t fp8q_cast_per_tensor(const void* x, int xdtype, int64_t n, int fmt, uint8_t* q, float* scale_inv,
                                    void* workspace, void* stream) {
     if (n < 0) return FP8Q_EINVAL;

@@ -527,6 +527,36 @@ k_cast_given_amax(const void* __restrict__ x, int64_t n, const float* __restrict
     tensor_cast_body<DT, FMT, VEC, K, NT, true>(x, n, scale, q);
 }
 
+// Pipeline p2p cast with the format chosen on the device (ColossalAI fp8.py,
+// cast_to_fp8_pipeline): from the finished amax, e5m2 when amax > 448 (the
+// e4m3fn maximum; a NaN amax fails the test) else e4m3fn; scale = 1 when
+// amax == 0, else that format's maximum / amax; scale_inv = 1 / scale.
+// Workgroup 0 publishes scale_inv and the format word (0 = e4m3fn,
+// 1 = e5m2).  Every workgroup takes the same decision from the same word, so
+// the branches are uniform.
+template <int DT, int FMT, bool VEC, int K, bool NT>
+__device__ __forceinline__ void pipeline_cast_body(const void* __restrict__ x, int64_t n, uint32_t ab,
+                                                   uint8_t* __restrict__ q, float* __restrict__ sinv_out,
+                                                   int32_t* __restrict__ fmt_out) {
+    const float amax = __uint_as_float(ab);
+    const float scale = (amax == 0.0f) ? 1.0f : Fp8Fmt<FMT>::max / amax;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        sinv_out[0] = 1.0f / scale;
+        fmt_out[0] = FMT;
+    }
+    if (needs_saturation(ab, scale)) tensor_cast_body<DT, FMT, VEC, K, NT, true>(x, n, scale, q);
+    else tensor_cast_body<DT, FMT, VEC, K, NT, false>(x, n, scale, q);
+}
+
+template <int DT, bool VEC, int K, bool NT>
+__global__ void __launch_bounds__(256)
+k_pipeline_cast(const void* __restrict__ x, int64_t n, const uint32_t* __restrict__ amax_bits,
+                uint8_t* __restrict__ q, float* __restrict__ sinv_out, int32_t* __restrict__ fmt_out) {
+    const uint32_t ab = amax_bits[0];
+    if (__uint_as_float(ab) > Fp8Fmt<kE4M3>::max) pipeline_cast_body<DT, kE5M2, VEC, K, NT>(x, n, ab, q, sinv_out, fmt_out);
+    else pipeline_cast_body<DT, kE4M3, VEC, K, NT>(x, n, ab, q, sinv_out, fmt_out);
+}
+
 // ===========================================================================
 // per-channel cast (ColossalAI fp8.py, cast_to_fp8 with per_channel_scale):
 // one 256-thread workgroup per row
@@ -623,8 +653,8 @@ template <int FMT, int MODE> __device__ __forceinline__ float flat_elem(uint8_t 
 }
 
 template <int FMT, int YDT, int MODE, bool VEC, int K, bool NT>
-__global__ void __launch_bounds__(256)
-k_dequant_flat(const uint8_t* __restrict__ q, int64_t n, const float* __restrict__ sinv, void* __restrict__ y) {
+__device__ __forceinline__ void dequant_flat_body(const uint8_t* __restrict__ q, int64_t n,
+                                                  const float* __restrict__ sinv, void* __restrict__ y) {
     constexpr int VE = LaneVE<YDT>::value;
     if constexpr (VEC) {
         const int64_t nvec = n / VE;
@@ -659,6 +689,31 @@ k_dequant_flat(const uint8_t* __restrict__ q, int64_t n, const float* __restrict
         for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
             store1<YDT>(y, i, flat_elem<FMT, MODE>(q[i], sinv, i));
     }
+}
+
+template <int FMT, int YDT, int MODE, bool VEC, int K, bool NT>
+__global__ void __launch_bounds__(256)
+k_dequant_flat(const uint8_t* __restrict__ q, int64_t n, const float* __restrict__ sinv, void* __restrict__ y) {
+    dequant_flat_body<FMT, YDT, MODE, VEC, K, NT>(q, n, sinv, y);
+}
+
+// Pipeline dequant (ColossalAI fp8.py, cast_from_fp8_pipeline): the code's
+// value converted to the output type (exact for every fp8 value) times the
+// binary32 scale_inv in binary32, rounded to the output type -- the per-tensor
+// dequant, with the format read from the device word the pipeline cast wrote,
+// so the host never waits for it.  Every workgroup reads the same word, so the
+// branch is uniform.  A word other than e4m3fn (0) or e5m2 (1) gives NaN
+// everywhere.
+template <int YDT, bool VEC, int K, bool NT>
+__global__ void __launch_bounds__(256)
+k_dequant_pipeline(const uint8_t* __restrict__ q, int64_t n, const float* __restrict__ sinv,
+                   const int32_t* __restrict__ fmt, void* __restrict__ y) {
+    const int32_t f = fmt[0];
+    if (f == kE4M3) dequant_flat_body<kE4M3, YDT, 0, VEC, K, NT>(q, n, sinv, y);
+    else if (f == kE5M2) dequant_flat_body<kE5M2, YDT, 0, VEC, K, NT>(q, n, sinv, y);
+    else
+        for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+            store1<YDT>(y, i, __builtin_nanf(""));
 }
 
 // per-channel: one workgroup per row, scale_inv[r] read once per row.

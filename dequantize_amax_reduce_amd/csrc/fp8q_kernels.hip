@@ -148,6 +148,29 @@ template <int FMT, int YDT> struct RunDequantFlat {
     }
 };
 
+template <int DT> void run_pipeline_cast(const void* x, int64_t n, const uint32_t* ws, uint8_t* q, float* sinv,
+                                         int32_t* fmt_out, hipStream_t st) {
+    constexpr int VE = LaneVE<DT>::value;
+    if (al(x, 16) && al(q, VE)) {
+        const int64_t chunks = (n / VE + kFlatK * 256 - 1) / (kFlatK * 256);
+        k_pipeline_cast<DT, true, kFlatK, kNT><<<grid(chunks), kThreads, 0, st>>>(x, n, ws, q, sinv, fmt_out);
+    } else {
+        k_pipeline_cast<DT, false, kFlatK, kNT><<<grid((n + 255) / 256), kThreads, 0, st>>>(x, n, ws, q, sinv,
+                                                                                             fmt_out);
+    }
+}
+
+template <int YDT> void run_dequant_pipeline(const uint8_t* q, int64_t n, const float* sinv, const int32_t* fmt,
+                                             void* y, hipStream_t st) {
+    constexpr int VE = LaneVE<YDT>::value;
+    if (al(q, VE) && al(y, 16)) {
+        const unsigned nb = grid((n / VE + kFlatK * 256 - 1) / (kFlatK * 256));
+        k_dequant_pipeline<YDT, true, kFlatK, kNT><<<nb, kThreads, 0, st>>>(q, n, sinv, fmt, y);
+    } else {
+        k_dequant_pipeline<YDT, false, kFlatK, kNT><<<grid((n + 255) / 256), kThreads, 0, st>>>(q, n, sinv, fmt, y);
+    }
+}
+
 template <int FMT, int YDT> struct RunDequantRows {
     static void run(const uint8_t* q, int64_t rows, int64_t cols, const float* sinv, void* y, hipStream_t st) {
         constexpr int VE = LaneVE<YDT>::value;
@@ -226,6 +249,20 @@ void launch_guard_amax(uint32_t* ws, hipStream_t st) { k_guard_amax<<<1, 64, 0, 
 void launch_cast_given_amax(const void* x, int dt, int64_t n, int fmt, const float* amax, uint8_t* q,
                             float* scale_out, hipStream_t st) {
     dispatch_dt_fmt<RunCastGivenAmax>(dt, fmt, x, n, amax, q, scale_out, st);
+}
+
+void launch_pipeline_cast(const void* x, int dt, int64_t n, const uint32_t* ws, uint8_t* q, float* sinv,
+                          int32_t* fmt_out, hipStream_t st) {
+    if (dt == kF32) run_pipeline_cast<kF32>(x, n, ws, q, sinv, fmt_out, st);
+    else if (dt == kBF16) run_pipeline_cast<kBF16>(x, n, ws, q, sinv, fmt_out, st);
+    else run_pipeline_cast<kF16>(x, n, ws, q, sinv, fmt_out, st);
+}
+
+void launch_dequant_pipeline(const uint8_t* q, int64_t n, const float* sinv, const int32_t* fmt, void* y, int ydt,
+                             hipStream_t st) {
+    if (ydt == kF32) run_dequant_pipeline<kF32>(q, n, sinv, fmt, y, st);
+    else if (ydt == kBF16) run_dequant_pipeline<kBF16>(q, n, sinv, fmt, y, st);
+    else run_dequant_pipeline<kF16>(q, n, sinv, fmt, y, st);
 }
 
 void launch_channel_cast(const void* x, int dt, int64_t rows, int64_t cols, int fmt, uint8_t* q, float* sinv,

@@ -27,6 +27,12 @@ void launch_guard_amax(uint32_t* ws, hipStream_t st);
 // cast with scale = fp8_max / amax[0] (caller-supplied amax); scale_out[0] = scale
 void launch_cast_given_amax(const void* x, int dt, int64_t n, int fmt, const float* amax, uint8_t* q,
                             float* scale_out, hipStream_t st);
+// pipeline cast with amax = ws[0]: the format chosen on the device, written to fmt_out[0]
+void launch_pipeline_cast(const void* x, int dt, int64_t n, const uint32_t* ws, uint8_t* q, float* sinv,
+                          int32_t* fmt_out, hipStream_t st);
+// per-tensor dequant with the format read from fmt[0] on the device
+void launch_dequant_pipeline(const uint8_t* q, int64_t n, const float* sinv, const int32_t* fmt, void* y, int ydt,
+                             hipStream_t st);
 // the scale-and-cast pass, with amax = ws[0]
 void launch_tensor_cast(const void* x, int dt, int64_t n, int fmt, const uint32_t* ws, uint8_t* q, float* sinv,
                         hipStream_t st);

@@ -211,6 +211,33 @@ fp8q_status_t fp8q_dequant_sum_requant(const uint8_t* q, int fmt, int64_t W, int
                                        int average, void* y, int ydtype, uint8_t* q_out, float* scale_inv_out,
                                        void* workspace, void* stream);
 
+/*
+ * Pipeline point-to-point cast with the fp8 format chosen from the data
+ * (ColossalAI fp8.py, cast_to_fp8_pipeline and cast_from_fp8_pipeline).  The
+ * page picks the format on the host after reading amax back; here the choice
+ * is made on the device and handed on in a device word, so neither side
+ * waits for the GPU.
+ *
+ * fp8q_cast_to_fp8_pipeline: amax = max(|min x|, |max x|) (NaN propagates);
+ *   fmt_out[0] = FP8Q_E5M2 if amax > 448 (the e4m3fn maximum), else
+ *   FP8Q_E4M3FN (also for a NaN amax); scale = 1 if amax == 0, else the chosen
+ *   format's maximum / amax (correctly rounded binary32 division);
+ *   q[i] = fp8(fp32(x[i]) * scale); scale_inv[0] = 1 / scale.  A NaN amax
+ *   gives a NaN scale and NaN codes; an infinite amax gives scale 0.
+ *   workspace: as for fp8q_cast_per_tensor.  n == 0 is read as amax 0
+ *   (the page's aminmax raises on an empty tensor): scale_inv[0] = 1,
+ *   fmt_out[0] = FP8Q_E4M3FN.  fmt_out is a device int32.
+ * fp8q_cast_from_fp8_pipeline: fmt is the device int32 the cast wrote;
+ *   y[i] = ydtype(ydtype(fp32(q[i])) * scale_inv[0]), the product taken in
+ *   binary32 (the fp8 value converts exactly to every ydtype, so this equals
+ *   fp8q_dequant_per_tensor in that format).  A format word other than 0 or 1
+ *   (the page raises TypeError) writes NaN to every y.  n == 0 is a no-op.
+ */
+fp8q_status_t fp8q_cast_to_fp8_pipeline(const void* x, int xdtype, int64_t n, uint8_t* q, float* scale_inv,
+                                        int32_t* fmt_out, void* workspace, void* stream);
+fp8q_status_t fp8q_cast_from_fp8_pipeline(const uint8_t* q, const int32_t* fmt, int64_t n, const float* scale_inv,
+                                          void* y, int ydtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

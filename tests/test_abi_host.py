@@ -111,6 +111,27 @@ def test_fsdp_hook_errors():
     assert d(None, E5, 0, None, None, F32, None) == fq.OK
 
 
+def test_pipeline_errors():
+    c = L.fp8q_cast_to_fp8_pipeline
+    ws, fw = P(A + 16384), P(A + 12288)
+    assert c(P(A), BF16, -1, P(A + 4096), P(A + 8192), fw, ws, None) == fq.EINVAL
+    assert c(P(A), 5, 16, P(A + 4096), P(A + 8192), fw, ws, None) == fq.EDTYPE
+    assert c(P(A), BF16, 16, P(A + 4096), P(A + 8192), None, ws, None) == fq.EINVAL          # no format word
+    assert c(P(A), BF16, 16, P(A + 4096), P(A + 8192), fw, None, None) == fq.EINVAL          # no workspace
+    assert c(P(A), BF16, 16, P(A + 4096), P(A + 8192), P(A + 12290), ws, None) == fq.EALIGN
+    assert c(P(A), BF16, 16, P(A + 4096), P(A + 8192), P(A + 8192), ws, None) == fq.EINVAL   # word = scale_inv
+    assert c(P(A), BF16, 16, P(A + 4096), P(A + 8192), P(A + 16400), ws, None) == fq.EINVAL  # word in workspace
+    assert c(P(A), BF16, 16, P(A + 4096), P(A + 8192), P(A + 8), ws, None) == fq.EINVAL      # word in x
+    d = L.fp8q_cast_from_fp8_pipeline
+    assert d(P(A), None, 16, P(A + 8192), P(A + 4096), BF16, None) == fq.EINVAL
+    assert d(P(A), P(A + 12290), 16, P(A + 8192), P(A + 4096), BF16, None) == fq.EALIGN
+    assert d(P(A), P(A + 4100), 16, P(A + 8192), P(A + 4096), BF16, None) == fq.EINVAL      # word in y
+    assert d(P(A), fw, 16, None, P(A + 4096), BF16, None) == fq.EINVAL
+    assert d(P(A), fw, 16, P(A + 8192), P(A + 4096), 7, None) == fq.EDTYPE
+    assert d(P(A), fw, -2, P(A + 8192), P(A + 4096), F32, None) == fq.EINVAL
+    assert d(None, None, 0, None, None, F32, None) == fq.OK
+
+
 def test_python_binding_rejects_host_tensors():
     import torch
     x = torch.zeros((2, 128), dtype=torch.bfloat16)

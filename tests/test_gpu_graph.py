@@ -22,6 +22,8 @@ def _run_all(b):
     fq.fp8q_cast_per_channel(b["x"], b["qc"], b["sc"], "e4m3fn")
     fq.fp8q_weight_dequant_block128(b["qw"], b["sw"], b["yw"])
     fq.fp8q_amax(b["x"], b["amax"])
+    fq.fp8q_cast_to_fp8_pipeline(b["x"], b["qp"], b["sp"], b["wp"], b["ws"])
+    fq.fp8q_cast_from_fp8_pipeline(b["qp"], b["wp"], b["sp"], b["yp"])
 
 
 def _outputs(b):
@@ -48,6 +50,10 @@ def test_graph_replays_match_eager():
         "sw": torch.from_numpy(sw).to(dev),
         "yw": torch.empty(cw.shape, dtype=torch.bfloat16, device=dev),
         "amax": torch.empty(1, dtype=torch.float32, device=dev),
+        "qp": torch.empty((R, C), dtype=torch.uint8, device=dev),
+        "sp": torch.empty(1, dtype=torch.float32, device=dev),
+        "wp": torch.empty(1, dtype=torch.int32, device=dev),
+        "yp": torch.empty((R, C), dtype=torch.bfloat16, device=dev),
     }
     _run_all(b)                       # eager reference (also warms up every kernel)
     torch.cuda.synchronize()
