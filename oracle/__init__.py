@@ -102,6 +102,8 @@ class OracleLib:
             "oracle_dequant_div_scale": (I, [P, I, I64, F, P, I]),
             "oracle_cast_to_fp8_pipeline": (I, [P, I, I64, P, P, P]),
             "oracle_cast_from_fp8_pipeline": (I, [P, I, I64, F, P, I]),
+            "oracle_cast_to_packed": (I, [P, I, I64, I, P]),
+            "oracle_dequant_packed": (I, [P, I, I64, I64, P, I]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -288,6 +290,24 @@ class OracleLib:
         y = _out(q.shape, ydtype)
         _check(self.L.oracle_cast_from_fp8_pipeline(_ptr(q), FORMATS[fmt], q.size, float(np.float32(scale_inv)),
                                                     _ptr(y), DTYPES[ydtype]), "cast_from_fp8_pipeline")
+        return y
+
+    def cast_to_packed(self, x, dtype: str, fmt: str) -> np.ndarray:
+        """-> uint8[4 + n]: binary32 scale_inv, then the n codes"""
+        x = _in(x, dtype)
+        slot = np.zeros(4 + x.size, dtype=np.uint8)
+        _check(self.L.oracle_cast_to_packed(_ptr(x), DTYPES[dtype], x.size, FORMATS[fmt], _ptr(slot)),
+               "cast_to_packed")
+        return slot
+
+    def dequant_packed(self, slots, fmt: str, W: int, n: int, ydtype: str):
+        """slots: uint8[W * (4 + n)] -> y [W, n]"""
+        slots = np.ascontiguousarray(np.asarray(slots, dtype=np.uint8).reshape(-1))
+        if slots.size != W * (4 + n):
+            raise ValueError("dequant_packed: slots must hold W * (4 + n) bytes")
+        y = _out((W, n), ydtype)
+        _check(self.L.oracle_dequant_packed(_ptr(slots), FORMATS[fmt], W, n, _ptr(y), DTYPES[ydtype]),
+               "dequant_packed")
         return y
 
 

@@ -471,3 +471,37 @@ int oracle_cast_from_fp8_pipeline(const uint8_t* q, int fmt, int64_t n, float sc
     for (int64_t i = 0; i < n; ++i) store_elem(y, ydtype, i, round_to(oracle_fp8_decode(q[i], fmt), ydtype) * scale_inv);
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* packed [scale_inv | payload] slots of the fp8 all-gather                  */
+/* ------------------------------------------------------------------------ */
+
+/* ColossalAI fp8.py, all_gather_fp8_lagacy / all_gather_fp8_ring: a rank's
+ * slot of the combined buffer is SCALE_BYTES = 4 bytes followed by n fp8
+ * codes; cast_to_fp8(x.view(-1), out=slot[4:]) writes the codes and the
+ * returned scale_inv is stored into slot[0:4] as a binary32 (host byte
+ * order, little-endian here). */
+int oracle_cast_to_packed(const void* x, int dtype, int64_t n, int fmt, uint8_t* slot) {
+    float scale_inv;
+    int rc = oracle_cast_per_tensor(x, dtype, n, fmt, slot + 4, &scale_inv);
+    if (rc != 0) return rc;
+    memcpy(slot, &scale_inv, 4);
+    return 0;
+}
+
+/* the receive side: slot w of the combined buffer starts at w * (4 + n);
+ * scale = slot[0:4] viewed as binary32, then cast_from_fp8(slot[4:], scale,
+ * input_type, out=output_list[w]) -- output w is y + w * n elements */
+int oracle_dequant_packed(const uint8_t* slots, int fmt, int64_t W, int64_t n, void* y, int ydtype) {
+    if (oracle_fpu_check()) return -9;
+    if (bad_dtype(ydtype) || bad_fmt(fmt)) return -2;
+    if (W < 0 || n < 0) return -1;
+    for (int64_t w = 0; w < W; ++w) {
+        const uint8_t* slot = slots + w * (4 + n);
+        float scale_inv;
+        memcpy(&scale_inv, slot, 4);
+        for (int64_t i = 0; i < n; ++i)
+            store_elem(y, ydtype, w * n + i, oracle_fp8_decode(slot[4 + i], fmt) * scale_inv);
+    }
+    return 0;
+}

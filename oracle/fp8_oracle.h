@@ -107,6 +107,12 @@ int oracle_cast_to_fp8_pipeline(const void* x, int dtype, int64_t n, uint8_t* q,
 /* y = ydtype(ydtype(fp32(q)) * scale_inv) */
 int oracle_cast_from_fp8_pipeline(const uint8_t* q, int fmt, int64_t n, float scale_inv, void* y, int ydtype);
 
+/* --- packed [scale_inv | payload] slots of the fp8 all-gather ---------- */
+/* slot[0:4] = binary32 scale_inv of cast_to_fp8(x) per tensor, slot[4:4+n] = its codes */
+int oracle_cast_to_packed(const void* x, int dtype, int64_t n, int fmt, uint8_t* slot);
+/* W slots at slots + w * (4 + n): y[w * n + i] = ydtype(fp32(code) * slot_w's scale_inv) */
+int oracle_dequant_packed(const uint8_t* slots, int fmt, int64_t W, int64_t n, void* y, int ydtype);
+
 #ifdef __cplusplus
 }
 #endif

@@ -695,4 +695,73 @@ def pin_pipeline_dequant_exact(L):
                     assert gv == want, (fmt, hex(int(c)), si, ydt)
 
 
+# ---------------------------------------------------------------------------
+# packed [scale_inv | payload] slots of the fp8 all-gather
+# ---------------------------------------------------------------------------
+
+def _page_cast_into(inp: torch.Tensor, fmt: str, out: torch.Tensor):
+    """cast_to_fp8(inp, per-tensor, out=out) as the page writes it, evaluated
+    by torch on the CPU (the scale as a true division, R8)."""
+    fp8_type = TORCH_FP8[fmt]
+    if inp.numel() == 0:
+        return torch.tensor([1.0])
+    m = inp.abs().max().float()
+    m = torch.where(m > 0, m, 1.0)
+    scale = torch.div(torch.tensor(torch.finfo(fp8_type).max, dtype=torch.float32), m)
+    scale_inv = 1.0 / scale
+    torch.mul(scale, inp.float(), out=out)
+    return torch.unsqueeze(scale_inv, 0)
+
+
+def pin_packed_slots_vs_torch(L):
+    """all_gather_fp8_lagacy's buffer handling, with W simulated ranks, run by
+    torch on the CPU: the combined buffer of W * (4 + n) bytes, chunked per
+    rank; each rank casts into slot[4:] and stores scale_inv into slot[0:4];
+    every slot is read back with slot[:4].clone().view(float) and
+    cast_from_fp8(..., out=...)."""
+    rng = np.random.Generator(np.random.PCG64(45))
+    for fmt in FORMATS:
+        for dtype in ("bf16", "f32", "f16"):
+            for W, n in ((1, 37), (3, 64), (4, 1000), (2, 0)):
+                xs = [torch.from_numpy((rng.standard_normal(n) * 10.0 ** rng.uniform(-3, 3)).astype(np.float32))
+                      .to(TORCH_HP[dtype]) for _ in range(W)]
+                if W > 2:
+                    xs[1].zero_()                               # a rank holding zeros
+                combined = torch.zeros(W * (4 + n), dtype=torch.uint8)
+                bufs = list(combined.chunk(W)) if n + 4 > 0 else []
+                got_slots = np.zeros(W * (4 + n), np.uint8)
+                for r in range(W):
+                    cur = bufs[r]
+                    sinv = _page_cast_into(xs[r].view(-1), fmt, cur[4:].view(TORCH_FP8[fmt]))
+                    cur[:4].view(torch.float)[0] = sinv
+                    host = _hp_bits(xs[r], dtype) if dtype != "f32" else xs[r].numpy()
+                    got_slots[r * (4 + n):(r + 1) * (4 + n)] = L.cast_to_packed(host, dtype, fmt)
+                assert np.array_equal(got_slots, combined.numpy()), (fmt, dtype, W, n)
+                for ydt in ("bf16", "f32", "f16"):
+                    want = torch.empty((W, n), dtype=TORCH_HP[ydt])
+                    for r in range(W):
+                        scale = bufs[r][:4].clone().view(torch.float)
+                        torch.mul(scale, bufs[r][4:].view(TORCH_FP8[fmt]).float(), out=want[r])
+                    got = np.asarray(L.dequant_packed(combined.numpy(), fmt, W, n, ydt))
+                    assert np.array_equal(got.view(np.uint8), _hp_bits(want, ydt).view(np.uint8)), (fmt, W, n, ydt)
+
+
+def pin_packed_layout_closed_form(L):
+    """Byte-level layout from the definition: an all-zero rank stores
+    scale_inv = fl32(1/fp8_max) as little-endian bytes at offset 0 and zero
+    codes after it; a rank holding [fp8_max, -1] stores scale_inv = 1 and the
+    codes of fp8_max and -1; an empty rank stores 1.0.  Reading two slots back
+    puts slot w's values at y[w]."""
+    for fmt, fmax, maxc, neg1 in (("e4m3fn", 448.0, 0x7E, 0xB8), ("e5m2", 57344.0, 0x7B, 0xBC)):
+        s = L.cast_to_packed(np.zeros(8, np.float32), "f32", fmt)
+        want_inv = X.f32(X.rn32(Fraction(1) / X.rn32(Fraction(int(fmax)))))
+        assert bytes(s[:4]) == np.float32(want_inv).tobytes() and not s[4:].any(), fmt
+        s2 = L.cast_to_packed(np.array([fmax, -1.0], np.float32), "f32", fmt)
+        assert list(s2) == [0x00, 0x00, 0x80, 0x3F, maxc, neg1], (fmt, list(s2))
+        assert list(L.cast_to_packed(np.zeros(0, np.float32), "f32", fmt)) == [0x00, 0x00, 0x80, 0x3F]
+        both = np.concatenate([s2, np.array([0, 0, 0, 0x40, maxc, neg1], np.uint8)])   # second scale_inv = 2
+        y = np.asarray(L.dequant_packed(both, fmt, 2, 2, "f32"))
+        assert y.tolist() == [[fmax, -1.0], [2 * fmax, -2.0]], (fmt, y)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -63,6 +63,16 @@ MUTANTS = [
      "    *scale_inv = amax / oracle_fp8_max(fmt);\n    *fmt_out = fmt;"),
     ("pipeline_dequant_scale_rounded", "round_to(oracle_fp8_decode(q[i], fmt), ydtype) * scale_inv);",
      "round_to(oracle_fp8_decode(q[i], fmt), ydtype) * round_to(scale_inv, ydtype));"),
+    ("packed_header_after_payload",
+     "int rc = oracle_cast_per_tensor(x, dtype, n, fmt, slot + 4, &scale_inv);\n    if (rc != 0) return rc;\n"
+     "    memcpy(slot, &scale_inv, 4);",
+     "int rc = oracle_cast_per_tensor(x, dtype, n, fmt, slot, &scale_inv);\n    if (rc != 0) return rc;\n"
+     "    memcpy(slot + n, &scale_inv, 4);"),
+    ("packed_slot_stride_without_header", "const uint8_t* slot = slots + w * (4 + n);",
+     "const uint8_t* slot = slots + w * n;"),
+    ("packed_header_read_as_scale", "oracle_fp8_decode(slot[4 + i], fmt) * scale_inv);",
+     "oracle_fp8_decode(slot[4 + i], fmt) / scale_inv);"),
+    ("packed_output_row_dropped", "store_elem(y, ydtype, w * n + i,", "store_elem(y, ydtype, i,"),
 ]
 
 
