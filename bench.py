@@ -357,6 +357,22 @@ def _other_rows(fq, W, np, torch, dev, st, iters, log, HE, act):
     timed("dequant_div_scale_e5m2_bf16_268435456 (FSDP hook)", n + 4 + n * 2, n,
           lambda: fq.fp8q_dequant_div_scale(qg, sg, yb, "e5m2", stream=st))
     del yb
+    # packed [scale_inv | payload] slots: the whole payload cast into one slot
+    # (codes 4 bytes past the header), and 8 slots of 2^25 read back to bf16
+    slot = torch.empty(4 + n, dtype=torch.uint8, device=dev)
+    timed("packed_cast_bf16_e5m2_268435456 (amax pass + cast pass, codes at slot+4)", 2 * n * 2 + n + 4, n,
+          lambda: fq.fp8q_cast_to_packed(gd, slot, ws, "e5m2", stream=st))
+    del slot
+    Wp, npk = 8, n // 8
+    comb = torch.empty(Wp * (4 + npk), dtype=torch.uint8, device=dev)
+    for r in range(Wp):
+        fq.fp8q_cast_to_packed(gd[r * npk:(r + 1) * npk], comb[r * (4 + npk):(r + 1) * (4 + npk)], ws, "e5m2",
+                               stream=st)
+    yp = torch.empty((Wp, npk), dtype=torch.bfloat16, device=dev)
+    timed("packed_dequant_e5m2_bf16_8x33554432 (all-gather receive side, one launch)",
+          Wp * (4 + npk) + Wp * npk * 2, Wp * npk,
+          lambda: fq.fp8q_dequant_packed(comb, Wp, npk, yp, "e5m2", stream=st))
+    del comb, yp
     del gd, qg, yg
 
     # reduce step of the fp8-compressed collectives: one rank of 8 holding the

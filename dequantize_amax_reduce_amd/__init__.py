@@ -61,6 +61,8 @@ def _load():
         "fp8q_dequant_div_scale": (I, [P, I, I64, P, P, I, P]),
         "fp8q_cast_to_fp8_pipeline": (I, [P, I, I64, P, P, P, P, P]),
         "fp8q_cast_from_fp8_pipeline": (I, [P, P, I64, P, P, I, P]),
+        "fp8q_cast_to_packed": (I, [P, I, I64, I, P, P, P]),
+        "fp8q_dequant_packed": (I, [P, I, I64, I64, P, I, P]),
         "fp8q_dequant_sum": (I, [P, I, I64, I64, P, I, P, I, P]),
         "fp8q_dequant_sum_requant": (I, [P, I, I64, I64, P, I, P, I, P, P, P, P]),
     }
@@ -77,7 +79,8 @@ ABI_FUNCTIONS = ("fp8q_abi_version", "fp8q_status_str", "fp8q_per_tensor_workspa
                  "fp8q_dequant_per_tensor", "fp8q_dequant_per_channel", "fp8q_dequant_per_group128",
                  "fp8q_weight_dequant_block128", "fp8q_dequant_sum", "fp8q_dequant_sum_requant",
                  "fp8q_amax_guarded", "fp8q_cast_with_amax", "fp8q_dequant_div_scale",
-                 "fp8q_cast_to_fp8_pipeline", "fp8q_cast_from_fp8_pipeline")
+                 "fp8q_cast_to_fp8_pipeline", "fp8q_cast_from_fp8_pipeline", "fp8q_cast_to_packed",
+                 "fp8q_dequant_packed")
 
 
 def header_functions() -> list:
@@ -304,6 +307,24 @@ def fp8q_cast_from_fp8_pipeline(q, fmt, scale_inv, y, stream=None) -> None:
            "fp8q_cast_from_fp8_pipeline")
 
 
+def fp8q_cast_to_packed(x, slot, workspace, fmt="e5m2", stream=None) -> None:
+    """slot: uint8 tensor of 4 + x.numel() bytes (4-byte aligned)."""
+    if slot.dtype != torch.uint8 or slot.numel() != 4 + x.numel():
+        raise ValueError("fp8q_cast_to_packed: slot must be uint8 with 4 + x.numel() bytes")
+    if workspace.numel() * workspace.element_size() < fp8q_per_tensor_workspace_bytes():
+        raise ValueError("fp8q_cast_to_packed: workspace too small")
+    _check(lib.fp8q_cast_to_packed(_dev(x, "x"), _hp_dtype(x, "x"), x.numel(), _fmt(fmt), _dev(slot, "slot"),
+                                   _dev(workspace, "workspace"), _stream(x, stream)), "fp8q_cast_to_packed")
+
+
+def fp8q_dequant_packed(slots, W, n, y, fmt="e5m2", stream=None) -> None:
+    """slots: uint8 tensor of W * (4 + n) bytes; y: W * n elements."""
+    if slots.dtype != torch.uint8 or slots.numel() != W * (4 + n) or y.numel() != W * n:
+        raise ValueError("fp8q_dequant_packed: slots must be uint8 with W * (4 + n) bytes and y W * n elements")
+    _check(lib.fp8q_dequant_packed(_dev(slots, "slots"), _fmt(fmt), W, n, _dev(y, "y"), _hp_dtype(y, "y"),
+                                   _stream(slots, stream)), "fp8q_dequant_packed")
+
+
 def _sum_args(q, scale_inv, y, fmt):
     f = _fp8(q, fmt, "q")
     if q.dim() != 2:
@@ -439,6 +460,26 @@ def cast_from_fp8_pipeline(inp, del_metadata=True) -> None:
     inp["hidden_states"] = y
     if del_metadata:
         del inp["fp8_scale"], inp["fp8_format"], inp["dtype"]
+
+
+def all_gather_pack(inp: torch.Tensor, combined: torch.Tensor, rank: int, world_size: int, fp8_format="e5m2"):
+    """The send side of all_gather_fp8_lagacy / all_gather_fp8_ring: cast inp
+    into rank's slot of the combined uint8 buffer (world_size * (4 + n)
+    bytes)."""
+    n = inp.numel()
+    if combined.numel() != world_size * (4 + n) or not 0 <= rank < world_size:
+        raise ValueError("all_gather_pack: combined must hold world_size * (4 + inp.numel()) bytes")
+    ws = torch.empty(fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32, device=inp.device)
+    fp8q_cast_to_packed(inp.reshape(-1), combined[rank * (4 + n):(rank + 1) * (4 + n)], ws, fp8_format)
+
+
+def all_gather_unpack(combined: torch.Tensor, world_size: int, shape, input_type: torch.dtype, fp8_format="e5m2"):
+    """The receive side: every slot of the combined buffer back to
+    input_type, as one [world_size, *shape] tensor (output_list[w] = out[w])."""
+    n = combined.numel() // world_size - 4
+    out = torch.empty((world_size, *shape), dtype=input_type, device=combined.device)
+    fp8q_dequant_packed(combined, world_size, n, out, fp8_format)
+    return out
 
 
 def weight_dequant(x: torch.Tensor, s: torch.Tensor, block_size: int = 128, ret_type=torch.bfloat16):

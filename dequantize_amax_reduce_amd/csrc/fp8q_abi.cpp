@@ -167,6 +167,41 @@ fp8q_status_t fp8q_cast_from_fp8_pipeline(const uint8_t* q, const int32_t* fmt, 
     return launched();
 }
 
+fp8q_status_t fp8q_cast_to_packed(const void* x, int xdtype, int64_t n, int fmt, uint8_t* slot, void* workspace,
+                                  void* stream) {
+    if (!valid_dtype(xdtype) || !valid_fmt(fmt)) return FP8Q_EDTYPE;
+    int64_t xbytes;
+    if (n < 0 || n > INT64_MAX - 4 || !mul_ok(n, esize(xdtype), &xbytes)) return FP8Q_EINVAL;
+    if ((n > 0 && !x) || !slot || !workspace) return FP8Q_EINVAL;
+    if ((x && !aligned(x, esize(xdtype))) || !aligned(slot, 4) || !aligned(workspace, 4)) return FP8Q_EALIGN;
+    const int64_t wsb = (int64_t)fp8q_per_tensor_workspace_bytes();
+    const Buf b[3] = {{x, xbytes}, {slot, 4 + n}, {workspace, wsb}};
+    if (any_overlap(b, 3)) return FP8Q_EINVAL;
+    if (n == 0) {  // cast_to_fp8's empty-tensor branch: scale_inv = 1.0 in the header
+        fp8q::launch_fill_f32((float*)slot, 1, 1.0f, S(stream));
+        return launched();
+    }
+    fp8q::launch_amax(x, xdtype, n, (uint32_t*)workspace, fp8q::kAmaxSlots, S(stream));
+    fp8q::launch_tensor_cast(x, xdtype, n, fmt, (const uint32_t*)workspace, slot + 4, (float*)slot, S(stream));
+    return launched();
+}
+
+fp8q_status_t fp8q_dequant_packed(const uint8_t* slots, int fmt, int64_t W, int64_t n, void* y, int ydtype,
+                                  void* stream) {
+    if (!valid_dtype(ydtype) || !valid_fmt(fmt)) return FP8Q_EDTYPE;
+    int64_t sbytes, ybytes;
+    if (W < 0 || n < 0 || n > INT64_MAX - 4 || !mul_ok(W, 4 + n, &sbytes) || !mul_ok(W, n, &ybytes) ||
+        !mul_ok(ybytes, esize(ydtype), &ybytes))
+        return FP8Q_EINVAL;
+    if (W == 0 || n == 0) return FP8Q_OK;
+    if (!slots || !y) return FP8Q_EINVAL;
+    if (!aligned(slots, 4) || !aligned(y, esize(ydtype)) || (W > 1 && n % 4 != 0)) return FP8Q_EALIGN;
+    const Buf b[2] = {{slots, sbytes}, {y, ybytes}};
+    if (any_overlap(b, 2)) return FP8Q_EINVAL;
+    fp8q::launch_dequant_packed(slots, fmt, W, n, y, ydtype, S(stream));
+    return launched();
+}
+
 fp8q_status_t fp8q_cast_per_tensor(const void* x, int xdtype, int64_t n, int fmt, uint8_t* q, float* scale_inv,
                                    void* workspace, void* stream) {
     if (n < 0) return FP8Q_EINVAL;

@@ -42,6 +42,10 @@ template <> struct Fp8Fmt<kE5M2> { static constexpr float max = 57344.0f; };   /
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));   // 16 bytes
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));   // 8 bytes
+// 8 bytes of fp8 codes at a 4-byte-aligned address (still one
+// global_load/store_dwordx2: gfx950 takes dword-aligned multi-dword global
+// accesses).  A packed slot's payload sits 4 bytes after its binary32 header.
+typedef unsigned int v2u_a4 __attribute__((ext_vector_type(2), aligned(4)));
 
 // elements per lane vector: the high-precision side is 16 bytes
 template <int DT> struct LaneVE { static constexpr int value = (DT == kF32) ? 4 : 8; };
@@ -149,9 +153,11 @@ template <bool NT> __device__ __forceinline__ v4u ld16(const void* p) {
     if constexpr (NT) return __builtin_nontemporal_load((const v4u*)p);
     else return *(const v4u*)p;
 }
-template <bool NT> __device__ __forceinline__ v2u ld8(const void* p) {
-    if constexpr (NT) return __builtin_nontemporal_load((const v2u*)p);
-    else return *(const v2u*)p;
+template <bool NT> __device__ __forceinline__ v2u ld8(const void* p) {  // p 4-byte aligned
+    v2u_a4 t;
+    if constexpr (NT) t = __builtin_nontemporal_load((const v2u_a4*)p);
+    else t = *(const v2u_a4*)p;
+    return v2u{t.x, t.y};
 }
 template <bool NT> __device__ __forceinline__ uint32_t ld4(const void* p) {
     if constexpr (NT) return __builtin_nontemporal_load((const uint32_t*)p);
@@ -161,9 +167,10 @@ template <bool NT> __device__ __forceinline__ void st16(void* p, v4u v) {
     if constexpr (NT) __builtin_nontemporal_store(v, (v4u*)p);
     else *(v4u*)p = v;
 }
-template <bool NT> __device__ __forceinline__ void st8(void* p, v2u v) {
-    if constexpr (NT) __builtin_nontemporal_store(v, (v2u*)p);
-    else *(v2u*)p = v;
+template <bool NT> __device__ __forceinline__ void st8(void* p, v2u v) {  // p 4-byte aligned
+    const v2u_a4 t = {v.x, v.y};
+    if constexpr (NT) __builtin_nontemporal_store(t, (v2u_a4*)p);
+    else *(v2u_a4*)p = t;
 }
 template <bool NT> __device__ __forceinline__ void st4(void* p, uint32_t v) {
     if constexpr (NT) __builtin_nontemporal_store(v, (uint32_t*)p);
@@ -311,7 +318,7 @@ template <int FMT> __device__ __forceinline__ void group_scale(uint32_t amax_bit
     sinv = amax / Fp8Fmt<FMT>::max;
 }
 
-// Vector path (x 16-B aligned, q aligned to VE bytes).  A group of 128
+// Vector path (x 16-B aligned, q 4-byte aligned).  A group of 128
 // elements is LPG = 128 / VE consecutive lanes (16 for bf16/fp16, 32 for
 // fp32); a workgroup sub-step covers 256 lane vectors = GPS whole groups, and
 // one workgroup trip covers a chunk of K sub-steps (K * GPS consecutive
@@ -500,7 +507,7 @@ __device__ __forceinline__ void tensor_cast_body(const void* __restrict__ x, int
     }
 }
 
-// VEC: x 16-B aligned and q aligned to VE bytes
+// VEC: x 16-B aligned and q 4-byte aligned
 template <int DT, int FMT, bool VEC, int K, bool NT>
 __global__ void __launch_bounds__(256)
 k_tensor_cast(const void* __restrict__ x, int64_t n, const uint32_t* __restrict__ amax_bits,
@@ -569,7 +576,7 @@ template <int FMT> __device__ __forceinline__ void channel_scale(uint32_t amax_b
     sinv = a / Fp8Fmt<FMT>::max;
 }
 
-// Register-resident rows: cols % VE == 0, x 16-B aligned, q VE-aligned and
+// Register-resident rows: cols % VE == 0, x 16-B aligned, q 4-byte aligned and
 // cols <= CPT * 256 * VE, so each thread keeps CPT lane vectors of the row in
 // VGPRs between the reduction and the cast (one HBM read per element).
 template <int DT, int FMT, int CPT, bool NT>
@@ -643,7 +650,7 @@ k_channel_2pass(const void* __restrict__ x, int64_t rows, int64_t cols, uint8_t*
 // MODE 3: per-tensor division by a scale (y = fp32(q) / scale[0], the FSDP
 // parameter hook's dequant; a correctly rounded division, not a product with
 // 1 / scale).
-// VEC: q aligned to VE bytes and y 16-B aligned; chunks of K sub-steps x 256
+// VEC: q 4-byte aligned and y 16-B aligned; chunks of K sub-steps x 256
 // lane vectors; the n % VE tail element-wise by workgroup 0.
 // one element of the flat dequant (the element-wise path and the tail)
 template <int FMT, int MODE> __device__ __forceinline__ float flat_elem(uint8_t c, const float* sinv, int64_t i) {
@@ -652,15 +659,18 @@ template <int FMT, int MODE> __device__ __forceinline__ float flat_elem(uint8_t 
     else return dec1<FMT>(c) * sinv[0];
 }
 
+// Chunks c0, c0 + cstride, ... of one flat tensor; `tail` names the one
+// workgroup that also converts the n % VE tail elements.
 template <int FMT, int YDT, int MODE, bool VEC, int K, bool NT>
 __device__ __forceinline__ void dequant_flat_body(const uint8_t* __restrict__ q, int64_t n,
-                                                  const float* __restrict__ sinv, void* __restrict__ y) {
+                                                  const float* __restrict__ sinv, void* __restrict__ y,
+                                                  int64_t c0, int64_t cstride, bool tail) {
     constexpr int VE = LaneVE<YDT>::value;
     if constexpr (VEC) {
         const int64_t nvec = n / VE;
         const int64_t nchunks = (nvec + K * 256 - 1) / (K * 256);
         const float s0 = (MODE != 2) ? sinv[0] : 0.0f;
-        for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+        for (int64_t c = c0; c < nchunks; c += cstride) {
             Fp8Vec<FMT, VE, NT> w[K];
 #pragma unroll
             for (int k = 0; k < K; ++k) {
@@ -684,9 +694,9 @@ __device__ __forceinline__ void dequant_flat_body(const uint8_t* __restrict__ q,
             }
         }
         const int64_t i = nvec * VE + threadIdx.x;
-        if (blockIdx.x == 0 && i < n) store1<YDT>(y, i, flat_elem<FMT, MODE>(q[i], sinv, i));
+        if (tail && i < n) store1<YDT>(y, i, flat_elem<FMT, MODE>(q[i], sinv, i));
     } else {
-        for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+        for (int64_t i = c0 * 256 + threadIdx.x; i < n; i += cstride * 256)
             store1<YDT>(y, i, flat_elem<FMT, MODE>(q[i], sinv, i));
     }
 }
@@ -694,7 +704,24 @@ __device__ __forceinline__ void dequant_flat_body(const uint8_t* __restrict__ q,
 template <int FMT, int YDT, int MODE, bool VEC, int K, bool NT>
 __global__ void __launch_bounds__(256)
 k_dequant_flat(const uint8_t* __restrict__ q, int64_t n, const float* __restrict__ sinv, void* __restrict__ y) {
-    dequant_flat_body<FMT, YDT, MODE, VEC, K, NT>(q, n, sinv, y);
+    dequant_flat_body<FMT, YDT, MODE, VEC, K, NT>(q, n, sinv, y, blockIdx.x, gridDim.x, blockIdx.x == 0);
+}
+
+// Dequant of W packed slots (ColossalAI fp8.py, all_gather_fp8_lagacy and
+// all_gather_fp8_ring, receive side): slot w starts at slots + w * (4 + n)
+// with its binary32 scale_inv in bytes 0..3 and n codes after it; output w
+// is y + w * n elements, y[w][i] = ydtype(fp32(code) * scale_inv_w).  Grid:
+// x = chunks within a slot, y = slots (looping when W exceeds gridDim.y).
+// VEC: the slots and every payload 4-byte aligned, every output row 16-B aligned.
+template <int FMT, int YDT, bool VEC, int K, bool NT>
+__global__ void __launch_bounds__(256)
+k_dequant_packed(const uint8_t* __restrict__ slots, int64_t W, int64_t n, void* __restrict__ y) {
+    constexpr int ESZ = ESize<YDT>::value;
+    for (int64_t w = blockIdx.y; w < W; w += gridDim.y) {
+        const uint8_t* slot = slots + w * (4 + n);
+        dequant_flat_body<FMT, YDT, 0, VEC, K, NT>(slot + 4, n, (const float*)slot, (char*)y + w * n * ESZ,
+                                                   blockIdx.x, gridDim.x, blockIdx.x == 0);
+    }
 }
 
 // Pipeline dequant (ColossalAI fp8.py, cast_from_fp8_pipeline): the code's
@@ -709,15 +736,16 @@ __global__ void __launch_bounds__(256)
 k_dequant_pipeline(const uint8_t* __restrict__ q, int64_t n, const float* __restrict__ sinv,
                    const int32_t* __restrict__ fmt, void* __restrict__ y) {
     const int32_t f = fmt[0];
-    if (f == kE4M3) dequant_flat_body<kE4M3, YDT, 0, VEC, K, NT>(q, n, sinv, y);
-    else if (f == kE5M2) dequant_flat_body<kE5M2, YDT, 0, VEC, K, NT>(q, n, sinv, y);
+    if (f == kE4M3) dequant_flat_body<kE4M3, YDT, 0, VEC, K, NT>(q, n, sinv, y, blockIdx.x, gridDim.x, blockIdx.x == 0);
+    else if (f == kE5M2)
+        dequant_flat_body<kE5M2, YDT, 0, VEC, K, NT>(q, n, sinv, y, blockIdx.x, gridDim.x, blockIdx.x == 0);
     else
         for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
             store1<YDT>(y, i, __builtin_nanf(""));
 }
 
 // per-channel: one workgroup per row, scale_inv[r] read once per row.
-// VEC: cols % VE == 0, q VE-aligned, y 16-B aligned.
+// VEC: cols % VE == 0, q 4-byte aligned, y 16-B aligned.
 template <int FMT, int YDT, bool VEC, bool NT>
 __global__ void __launch_bounds__(256)
 k_dequant_rows(const uint8_t* __restrict__ q, int64_t rows, int64_t cols, const float* __restrict__ sinv,
@@ -766,7 +794,7 @@ k_dequant_rows(const uint8_t* __restrict__ q, int64_t rows, int64_t cols, const 
 // vector t (+ 256 u) of a row; its scale_inv is the cached scalar
 // s[(row / 128) * nbn + col / 128] (at most 4 distinct values per wave
 // instruction).  U lane vectors per row and all RB rows are loaded before
-// the first convert.  Requires N % VE == 0, q VE-aligned, y 16-B aligned.
+// the first convert.  Requires N % VE == 0, q 4-byte aligned, y 16-B aligned.
 template <int FMT, int YDT, int RB, int U, bool NT>
 __global__ void __launch_bounds__(256)
 k_block128_rows(const uint8_t* __restrict__ q, int64_t M, int64_t N, const float* __restrict__ sinv,
@@ -814,7 +842,7 @@ __device__ __forceinline__ uint32_t div_u32(uint32_t n, DivU32 d) {
 // sub-steps x 256 lane vectors, exactly like the flat dequant; each lane finds
 // its row by an invariant-divisor division of its lane-vector index by the
 // lane vectors per row (vpr), and reads its tile's scale_inv from the cached
-// scale row.  Requires N % VE == 0, q VE-aligned, y 16-B aligned and
+// scale row.  Requires N % VE == 0, q 4-byte aligned, y 16-B aligned and
 // M * N / VE < 2^32.
 template <int FMT, int YDT, int K, bool NT>
 __global__ void __launch_bounds__(256)
@@ -920,7 +948,7 @@ template <int YDT, int VE> __device__ __forceinline__ void average_vec(float* ac
 // y[i] = sum over the W chunks of q (chunk w at q + w * n) in chunk order,
 // divided by W when `average`; with AMAX, max |y| is folded into the amax
 // slots (one atomic max per workgroup, slot blockIdx.x % nslots).
-// VEC: n % VE == 0, q VE-aligned, y 16-B aligned.  A thread owns KV lane
+// VEC: n % VE == 0, q 4-byte aligned, y 16-B aligned.  A thread owns KV lane
 // vectors 256 apart; chunk loads are issued four chunks at a time for all
 // of them before their terms are added.
 template <int FMT, int YDT, bool VEC, bool AMAX, bool NT, int KV>

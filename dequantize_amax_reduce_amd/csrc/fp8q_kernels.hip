@@ -62,7 +62,7 @@ void dispatch_fmt_ydt(int fmt, int ydt, A... a) {
 template <int DT, int FMT> struct RunGroup128 {
     static void run(const void* x, int64_t groups, uint8_t* q, float* sinv, hipStream_t st) {
         constexpr int VE = LaneVE<DT>::value;
-        if (al(x, 16) && al(q, VE)) {
+        if (al(x, 16) && al(q, 4)) {
             constexpr int64_t CH = kGroupK * (256 / (128 / VE));
             k_group128<DT, FMT, kGroupK, kNT><<<grid((groups + CH - 1) / CH), kThreads, 0, st>>>(x, q, sinv, groups);
         } else {
@@ -74,7 +74,7 @@ template <int DT, int FMT> struct RunGroup128 {
 template <int DT, int FMT> struct RunTensorCast {
     static void run(const void* x, int64_t n, const uint32_t* ws, uint8_t* q, float* sinv, hipStream_t st) {
         constexpr int VE = LaneVE<DT>::value;
-        if (al(x, 16) && al(q, VE)) {
+        if (al(x, 16) && al(q, 4)) {
             const int64_t chunks = (n / VE + kFlatK * 256 - 1) / (kFlatK * 256);
             k_tensor_cast<DT, FMT, true, kFlatK, kNT><<<grid(chunks), kThreads, 0, st>>>(x, n, ws, q, sinv);
         } else {
@@ -86,7 +86,7 @@ template <int DT, int FMT> struct RunTensorCast {
 template <int DT, int FMT> struct RunCastGivenAmax {
     static void run(const void* x, int64_t n, const float* amax, uint8_t* q, float* scale_out, hipStream_t st) {
         constexpr int VE = LaneVE<DT>::value;
-        if (al(x, 16) && al(q, VE)) {
+        if (al(x, 16) && al(q, 4)) {
             const int64_t chunks = (n / VE + kFlatK * 256 - 1) / (kFlatK * 256);
             k_cast_given_amax<DT, FMT, true, kFlatK, kNT><<<grid(chunks), kThreads, 0, st>>>(x, n, amax, q, scale_out);
         } else {
@@ -99,7 +99,7 @@ template <int DT, int FMT> struct RunCastGivenAmax {
 template <int DT, int FMT> struct RunChannel {
     static void run(const void* x, int64_t rows, int64_t cols, uint8_t* q, float* sinv, hipStream_t st) {
         constexpr int VE = LaneVE<DT>::value;
-        const bool vec = (cols % VE == 0) && al(x, 16) && al(q, VE);
+        const bool vec = (cols % VE == 0) && al(x, 16) && al(q, 4);
         const int64_t nvec = cols / VE;
         const unsigned nb = grid(rows);
         if (vec && nvec <= 256) k_channel_reg<DT, FMT, 1, kNT><<<nb, kThreads, 0, st>>>(x, rows, cols, q, sinv);
@@ -133,7 +133,7 @@ template <int DT> void run_amax(const void* x, int64_t n, uint32_t* ws, int nslo
 template <int FMT, int YDT> struct RunDequantFlat {
     static void run(int mode, const uint8_t* q, int64_t n, const float* sinv, void* y, hipStream_t st) {
         constexpr int VE = LaneVE<YDT>::value;
-        const bool vec = al(q, VE) && al(y, 16);
+        const bool vec = al(q, 4) && al(y, 16);
         const unsigned nb = vec ? grid((n / VE + kFlatK * 256 - 1) / (kFlatK * 256)) : grid((n + 255) / 256);
         if (mode == 0) {
             if (vec) k_dequant_flat<FMT, YDT, 0, true, kFlatK, kNT><<<nb, kThreads, 0, st>>>(q, n, sinv, y);
@@ -151,7 +151,7 @@ template <int FMT, int YDT> struct RunDequantFlat {
 template <int DT> void run_pipeline_cast(const void* x, int64_t n, const uint32_t* ws, uint8_t* q, float* sinv,
                                          int32_t* fmt_out, hipStream_t st) {
     constexpr int VE = LaneVE<DT>::value;
-    if (al(x, 16) && al(q, VE)) {
+    if (al(x, 16) && al(q, 4)) {
         const int64_t chunks = (n / VE + kFlatK * 256 - 1) / (kFlatK * 256);
         k_pipeline_cast<DT, true, kFlatK, kNT><<<grid(chunks), kThreads, 0, st>>>(x, n, ws, q, sinv, fmt_out);
     } else {
@@ -163,7 +163,7 @@ template <int DT> void run_pipeline_cast(const void* x, int64_t n, const uint32_
 template <int YDT> void run_dequant_pipeline(const uint8_t* q, int64_t n, const float* sinv, const int32_t* fmt,
                                              void* y, hipStream_t st) {
     constexpr int VE = LaneVE<YDT>::value;
-    if (al(q, VE) && al(y, 16)) {
+    if (al(q, 4) && al(y, 16)) {
         const unsigned nb = grid((n / VE + kFlatK * 256 - 1) / (kFlatK * 256));
         k_dequant_pipeline<YDT, true, kFlatK, kNT><<<nb, kThreads, 0, st>>>(q, n, sinv, fmt, y);
     } else {
@@ -171,10 +171,24 @@ template <int YDT> void run_dequant_pipeline(const uint8_t* q, int64_t n, const 
     }
 }
 
+template <int FMT, int YDT> struct RunDequantPacked {
+    static void run(const uint8_t* slots, int64_t W, int64_t n, void* y, hipStream_t st) {
+        constexpr int VE = LaneVE<YDT>::value;
+        constexpr int64_t ESZ = ESize<YDT>::value;
+        // payloads 4-byte aligned (slots aligned, and n % 4 == 0 when W > 1,
+        // both checked by the caller) and every output row 16-B aligned
+        const bool vec = al(slots, 4) && al(y, 16) && (W == 1 || (n * ESZ) % 16 == 0);
+        const int64_t per_slot = vec ? (n / VE + kFlatK * 256 - 1) / (kFlatK * 256) : (n + 255) / 256;
+        const dim3 g(grid(per_slot), (unsigned)std::min<int64_t>(W, 65535));
+        if (vec) k_dequant_packed<FMT, YDT, true, kFlatK, kNT><<<g, kThreads, 0, st>>>(slots, W, n, y);
+        else k_dequant_packed<FMT, YDT, false, kFlatK, kNT><<<g, kThreads, 0, st>>>(slots, W, n, y);
+    }
+};
+
 template <int FMT, int YDT> struct RunDequantRows {
     static void run(const uint8_t* q, int64_t rows, int64_t cols, const float* sinv, void* y, hipStream_t st) {
         constexpr int VE = LaneVE<YDT>::value;
-        const bool vec = (cols % VE == 0) && al(q, VE) && al(y, 16);
+        const bool vec = (cols % VE == 0) && al(q, 4) && al(y, 16);
         if (vec) k_dequant_rows<FMT, YDT, true, kNT><<<grid(rows), kThreads, 0, st>>>(q, rows, cols, sinv, y);
         else k_dequant_rows<FMT, YDT, false, kNT><<<grid(rows), kThreads, 0, st>>>(q, rows, cols, sinv, y);
     }
@@ -185,7 +199,7 @@ template <int FMT, int YDT> struct RunBlock128 {
         constexpr int VE = LaneVE<YDT>::value;
         const int64_t nbn = (N + 127) / 128;
         const int64_t nvec = M * (N / VE);
-        if (N % VE == 0 && al(q, VE) && al(y, 16) && nvec < (int64_t(1) << 32)) {
+        if (N % VE == 0 && al(q, 4) && al(y, 16) && nvec < (int64_t(1) << 32)) {
             // invariant-divisor magic for dividing a lane-vector index by N / VE
             const uint32_t vpr = (uint32_t)(N / VE);
             int l = 0;
@@ -193,7 +207,7 @@ template <int FMT, int YDT> struct RunBlock128 {
             const DivU32 dv{(uint32_t)((((uint64_t(1) << 32) * ((uint64_t(1) << l) - vpr)) / vpr) + 1), l};
             const int64_t chunks = (nvec + kBlockK * 256 - 1) / (kBlockK * 256);
             k_block128_flat<FMT, YDT, kBlockK, kNT><<<grid(chunks), kThreads, 0, st>>>(q, nvec, sinv, y, nbn, vpr, dv);
-        } else if (N % VE == 0 && al(q, VE) && al(y, 16)) {
+        } else if (N % VE == 0 && al(q, 4) && al(y, 16)) {
             k_block128_rows<FMT, YDT, kBlockRows, kBlockU, kNT>
                 <<<grid((M + kBlockRows - 1) / kBlockRows), kThreads, 0, st>>>(q, M, N, sinv, y, nbn);
         } else {
@@ -207,7 +221,7 @@ template <int FMT, int YDT> struct RunDequantSum {
                     hipStream_t st) {
         constexpr int VE = LaneVE<YDT>::value;
         constexpr int KV = kSumKV;
-        const bool vec = (n % VE == 0) && al(q, VE) && al(y, 16);
+        const bool vec = (n % VE == 0) && al(q, 4) && al(y, 16);
         const int64_t units = vec ? (n / VE + 256 * KV - 1) / (256 * KV) : (n + 255) / 256;
         if (ws) {
             k_fill_slots<<<1, 64, 0, st>>>(ws, kAmaxSlots, 0u);
@@ -263,6 +277,10 @@ void launch_dequant_pipeline(const uint8_t* q, int64_t n, const float* sinv, con
     if (ydt == kF32) run_dequant_pipeline<kF32>(q, n, sinv, fmt, y, st);
     else if (ydt == kBF16) run_dequant_pipeline<kBF16>(q, n, sinv, fmt, y, st);
     else run_dequant_pipeline<kF16>(q, n, sinv, fmt, y, st);
+}
+
+void launch_dequant_packed(const uint8_t* slots, int fmt, int64_t W, int64_t n, void* y, int ydt, hipStream_t st) {
+    dispatch_fmt_ydt<RunDequantPacked>(fmt, ydt, slots, W, n, y, st);
 }
 
 void launch_channel_cast(const void* x, int dt, int64_t rows, int64_t cols, int fmt, uint8_t* q, float* sinv,

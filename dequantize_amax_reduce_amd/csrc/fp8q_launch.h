@@ -27,6 +27,8 @@ void launch_guard_amax(uint32_t* ws, hipStream_t st);
 // cast with scale = fp8_max / amax[0] (caller-supplied amax); scale_out[0] = scale
 void launch_cast_given_amax(const void* x, int dt, int64_t n, int fmt, const float* amax, uint8_t* q,
                             float* scale_out, hipStream_t st);
+// dequant of W packed [scale_inv | n codes] slots into y [W][n]
+void launch_dequant_packed(const uint8_t* slots, int fmt, int64_t W, int64_t n, void* y, int ydt, hipStream_t st);
 // pipeline cast with amax = ws[0]: the format chosen on the device, written to fmt_out[0]
 void launch_pipeline_cast(const void* x, int dt, int64_t n, const uint32_t* ws, uint8_t* q, float* sinv,
                           int32_t* fmt_out, hipStream_t st);

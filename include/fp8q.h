@@ -238,6 +238,30 @@ fp8q_status_t fp8q_cast_to_fp8_pipeline(const void* x, int xdtype, int64_t n, ui
 fp8q_status_t fp8q_cast_from_fp8_pipeline(const uint8_t* q, const int32_t* fmt, int64_t n, const float* scale_inv,
                                           void* y, int ydtype, void* stream);
 
+/*
+ * Packed [scale_inv | payload] slots of the fp8 all-gather (ColossalAI
+ * fp8.py, all_gather_fp8_lagacy and all_gather_fp8_ring).  The combined
+ * buffer holds one slot per rank; slot w starts at byte w * (4 + n) and is
+ * SCALE_BYTES = 4 bytes of binary32 scale_inv (little-endian) followed by the
+ * rank's n fp8 codes.  The exchange itself is the caller's (e.g. RCCL
+ * all-gather, or the ring's batched send/recv).
+ *
+ * fp8q_cast_to_packed: cast_to_fp8(x, per tensor) into one slot: codes at
+ *   slot + 4, scale_inv at slot[0..3]; same numerics, stages and workspace
+ *   as fp8q_cast_per_tensor.  slot holds 4 + n bytes and must be 4-byte
+ *   aligned (the page views slot[0:4] as a float).  n == 0 writes 1.0.
+ * fp8q_dequant_packed: the receive side for W slots in one launch: output w
+ *   is y + w * n elements, y[w][i] = ydtype(fp32(code_w[i]) * scale_inv_w).
+ *   slots must be 4-byte aligned and, when W > 1, n % 4 == 0 (otherwise
+ *   FP8Q_EALIGN: the page's float view of a later slot's header needs it).
+ *   W == 1 dequantizes one slot, the ring's per-step cast.  W == 0 or
+ *   n == 0 is a no-op.
+ */
+fp8q_status_t fp8q_cast_to_packed(const void* x, int xdtype, int64_t n, int fmt, uint8_t* slot, void* workspace,
+                                  void* stream);
+fp8q_status_t fp8q_dequant_packed(const uint8_t* slots, int fmt, int64_t W, int64_t n, void* y, int ydtype,
+                                  void* stream);
+
 #ifdef __cplusplus
 }
 #endif

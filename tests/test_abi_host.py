@@ -132,6 +132,34 @@ def test_pipeline_errors():
     assert d(None, None, 0, None, None, F32, None) == fq.OK
 
 
+def test_packed_errors():
+    c = L.fp8q_cast_to_packed
+    ws = P(A + 65536)
+    assert c(P(A), BF16, -1, E5, P(A + 4096), ws, None) == fq.EINVAL
+    assert c(P(A), BF16, 2 ** 63 - 2, E5, P(A + 4096), ws, None) == fq.EINVAL           # 4 + n overflows
+    assert c(P(A), 9, 16, E5, P(A + 4096), ws, None) == fq.EDTYPE
+    assert c(P(A), BF16, 16, 2, P(A + 4096), ws, None) == fq.EDTYPE
+    assert c(P(A), BF16, 16, E5, None, ws, None) == fq.EINVAL
+    assert c(P(A), BF16, 16, E5, P(A + 4096), None, None) == fq.EINVAL
+    assert c(None, BF16, 16, E5, P(A + 4096), ws, None) == fq.EINVAL
+    assert c(P(A), BF16, 16, E5, P(A + 4098), ws, None) == fq.EALIGN                    # slot not 4-aligned
+    assert c(P(A), BF16, 16, E5, P(A + 16), ws, None) == fq.EINVAL                      # slot overlaps x
+    assert c(P(A), BF16, 16, E5, P(A + 4096), P(A + 4100), None) == fq.EINVAL           # workspace in slot
+    d = L.fp8q_dequant_packed
+    assert d(P(A), E5, -1, 16, P(A + 8192), BF16, None) == fq.EINVAL
+    assert d(P(A), E5, 2, -16, P(A + 8192), BF16, None) == fq.EINVAL
+    assert d(P(A), E5, 2 ** 62, 2 ** 62, P(A + 8192), BF16, None) == fq.EINVAL          # overflow
+    assert d(P(A), 3, 2, 16, P(A + 8192), BF16, None) == fq.EDTYPE
+    assert d(P(A), E5, 2, 16, P(A + 8192), 4, None) == fq.EDTYPE
+    assert d(P(A), E5, 2, 6, P(A + 8192), BF16, None) == fq.EALIGN                      # n % 4 with W > 1
+    assert d(P(A + 2), E5, 1, 16, P(A + 8192), BF16, None) == fq.EALIGN
+    assert d(P(A), E5, 1, 16, P(A + 8193), BF16, None) == fq.EALIGN
+    assert d(None, E5, 2, 16, P(A + 8192), BF16, None) == fq.EINVAL
+    assert d(P(A), E5, 2, 16, P(A + 20), BF16, None) == fq.EINVAL                       # y overlaps the slots
+    assert d(None, E5, 0, 16, None, BF16, None) == fq.OK
+    assert d(None, E5, 3, 0, None, BF16, None) == fq.OK
+
+
 def test_python_binding_rejects_host_tensors():
     import torch
     x = torch.zeros((2, 128), dtype=torch.bfloat16)

@@ -24,6 +24,11 @@ def _run_all(b):
     fq.fp8q_amax(b["x"], b["amax"])
     fq.fp8q_cast_to_fp8_pipeline(b["x"], b["qp"], b["sp"], b["wp"], b["ws"])
     fq.fp8q_cast_from_fp8_pipeline(b["qp"], b["wp"], b["sp"], b["yp"])
+    n = b["x"].numel() // 2
+    for r in range(2):
+        fq.fp8q_cast_to_packed(b["x"].reshape(-1)[r * n:(r + 1) * n], b["pk"][r * (4 + n):(r + 1) * (4 + n)],
+                               b["ws"], "e5m2")
+    fq.fp8q_dequant_packed(b["pk"], 2, n, b["ypk"], "e5m2")
 
 
 def _outputs(b):
@@ -54,6 +59,8 @@ def test_graph_replays_match_eager():
         "sp": torch.empty(1, dtype=torch.float32, device=dev),
         "wp": torch.empty(1, dtype=torch.int32, device=dev),
         "yp": torch.empty((R, C), dtype=torch.bfloat16, device=dev),
+        "pk": torch.empty(2 * (4 + R * C // 2), dtype=torch.uint8, device=dev),
+        "ypk": torch.empty((R, C), dtype=torch.bfloat16, device=dev),
     }
     _run_all(b)                       # eager reference (also warms up every kernel)
     torch.cuda.synchronize()
