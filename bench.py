@@ -171,6 +171,10 @@ def main():
         "group128_cast_bf16_e4m3fn_16384x7168": _row(cast_bytes, cast_us, R * C),
         "group128_dequant_e4m3fn_bf16_16384x7168": _row(deq_bytes, deq_us, R * C),
     }
+    # round-trip error of the step's own output (outside the timed region)
+    b0 = sets[(args.steps - 1) % NSETS]                 # written by the last timed step
+    roundtrip = {"group128_e4m3fn_bf16_16384x7168": _roundtrip_err(
+        torch, b0["x"], b0["y"], b0["s"].repeat_interleave(128, dim=1), "e4m3fn", out_rounding="bf16")}
 
     # ------------------------------------------------------------------ copy calibration
     # a plain device copy of known size: the reference for the HBM counters and a
@@ -195,7 +199,7 @@ def main():
 
     # ------------------------------------------------------------------ other rows
     if not args.no_rows:
-        rows.update(_other_rows(fq, W, np, torch, dev, st, args.rows_iters, log, HE, x0))
+        rows.update(_other_rows(fq, W, np, torch, dev, st, args.rows_iters, log, HE, x0, roundtrip))
     del x0
     HE.close()
 
@@ -238,13 +242,14 @@ def main():
         },
         "copy_reference": {"bytes": 2 * cp_n, "us": round(copy_us, 3), "gbps": round(copy_gbps, 1)},
         "cpu_baseline": cpu,
+        "roundtrip_rel_err": roundtrip,
         "rows": rows,
     }
     print(json.dumps(out), flush=True)
 
 
 KERNEL_SOURCES = ("dequantize_amax_reduce_amd/csrc/fp8q_device.h", "dequantize_amax_reduce_amd/csrc/fp8q_kernels.hip")
-TRAFFIC_SUMMARY = "profiles/k_group128__activation_16384x7168__hbm_traffic.md"
+TRAFFIC_SUMMARY = "profiles/fp8q_kernels__bench_workloads__hbm_traffic.md"
 
 
 def kernel_source_hash() -> str:
@@ -283,7 +288,32 @@ def _row(nbytes, us_list, elems):
             "elements_per_s": round(elems / (avg * 1e-6), 1)}
 
 
-def _other_rows(fq, W, np, torch, dev, st, iters, log, HE, act):
+FP8_MIN_NORMAL = {"e4m3fn": 2.0 ** -6, "e5m2": 2.0 ** -14}
+FP8_MANT_BITS = {"e4m3fn": 3, "e5m2": 2}
+
+
+def _roundtrip_err(torch, x, y, sinv_elem, fmt, out_rounding="f32"):
+    """Largest |y - x| / |x| over the elements whose scaled value |x| / scale_inv
+    lies in the fp8 format's normal range (below it the format's spacing is
+    absolute, not relative).  The stated tolerance is half an fp8 ulp,
+    2^-(mantissa bits + 1): 2^-4 for e4m3fn, 2^-3 for e5m2; a bf16 output
+    adds at most one bf16 rounding (2^-8 relative) on top."""
+    xd = x.reshape(-1).double()
+    yd = y.reshape(-1).double()
+    sd = sinv_elem.reshape(-1).double()                  # one value per element, or one for all
+    m = (xd.abs() / sd) >= FP8_MIN_NORMAL[fmt]
+    rel = ((yd - xd).abs() / xd.abs())[m]
+    tol = 2.0 ** -(FP8_MANT_BITS[fmt] + 1)
+    out = {"max_rel_err": float(rel.max().item()) if rel.numel() else 0.0, "tolerance": tol,
+           "elements_checked": int(m.sum().item()), "elements": int(xd.numel())}
+    if out_rounding == "bf16":
+        out["tolerance_with_output_rounding"] = (1 + tol) * (1 + 2.0 ** -8) - 1
+    out["within"] = out["max_rel_err"] <= out.get("tolerance_with_output_rounding", tol)
+    del xd, yd, sd, m, rel
+    return out
+
+
+def _other_rows(fq, W, np, torch, dev, st, iters, log, HE, act, roundtrip):
     """Each remaining hot-path operation on its own workload.  Between
     iterations, outside the events, a 1 GiB read (a max-reduction) replaces the
     256 MB Infinity Cache contents with clean lines, so inputs come from HBM
@@ -348,6 +378,8 @@ def _other_rows(fq, W, np, torch, dev, st, iters, log, HE, act):
           lambda: fq.fp8q_cast_per_tensor(gd, qg, sg, ws, "e5m2", stream=st))
     timed("per_tensor_dequant_e5m2_f32_268435456", n + 4 + n * 4, n,
           lambda: fq.fp8q_dequant_per_tensor(qg, sg, yg, "e5m2", stream=st))
+    torch.cuda.synchronize()
+    roundtrip["per_tensor_e5m2_f32_268435456"] = _roundtrip_err(torch, gd, yg, sg, "e5m2")
     # FSDP parameter hook's parts on the same shard: cast with a given (all-reduced)
     # amax, dequant by division by the scale
     yb = torch.empty(n, dtype=torch.bfloat16, device=dev)

@@ -951,7 +951,7 @@ template <int YDT, int VE> __device__ __forceinline__ void average_vec(float* ac
 // VEC: n % VE == 0, q 4-byte aligned, y 16-B aligned.  A thread owns KV lane
 // vectors 256 apart; chunk loads are issued four chunks at a time for all
 // of them before their terms are added.
-template <int FMT, int YDT, bool VEC, bool AMAX, bool NT, int KV>
+template <int FMT, int YDT, bool VEC, bool AMAX, bool NT, int KV, bool NTY = NT>
 __global__ void __launch_bounds__(256)
 k_dequant_sum(const uint8_t* __restrict__ q, int64_t W, int64_t n, const float* __restrict__ sinv, int average,
               void* __restrict__ y, uint32_t* __restrict__ amax_bits, int nslots) {
@@ -992,7 +992,7 @@ k_dequant_sum(const uint8_t* __restrict__ q, int64_t W, int64_t n, const float* 
 #pragma unroll
                     for (int k = 0; k < VE; ++k) m = umax(m, __float_as_uint(acc[u][k]) & 0x7FFFFFFFu);
                 }
-                store_out16<YDT, NT>(y, vi * VE, acc[u]);
+                store_out16<YDT, NTY>(y, vi * VE, acc[u]);
             }
         }
     }

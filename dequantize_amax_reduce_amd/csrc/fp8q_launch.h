@@ -20,8 +20,9 @@ void launch_fill_f32(float* p, int64_t n, float v, hipStream_t st);
 constexpr int kAmaxSlots = 64;
 constexpr int kAmaxSlotStride = 32;
 // clears the nslots amax slots of ws, folds max |x| (binary32 bits) into them and
-// leaves the result in ws[0]; n may be 0
-void launch_amax(const void* x, int dt, int64_t n, uint32_t* ws, int nslots, hipStream_t st);
+// leaves the result in ws[0]; n may be 0.  cached: x is read through the
+// caches because a cast pass over the same x follows.
+void launch_amax(const void* x, int dt, int64_t n, uint32_t* ws, int nslots, hipStream_t st, bool cached = false);
 // where(amax > 0, amax, 1) applied to ws[0]
 void launch_guard_amax(uint32_t* ws, hipStream_t st);
 // cast with scale = fp8_max / amax[0] (caller-supplied amax); scale_out[0] = scale
@@ -36,8 +37,10 @@ void launch_pipeline_cast(const void* x, int dt, int64_t n, const uint32_t* ws, 
 void launch_dequant_pipeline(const uint8_t* q, int64_t n, const float* sinv, const int32_t* fmt, void* y, int ydt,
                              hipStream_t st);
 // the scale-and-cast pass, with amax = ws[0]
+// (cached: ordinary instead of non-temporal memory accesses, for an input
+// the previous kernel just wrote)
 void launch_tensor_cast(const void* x, int dt, int64_t n, int fmt, const uint32_t* ws, uint8_t* q, float* sinv,
-                        hipStream_t st);
+                        hipStream_t st, bool cached = false);
 void launch_channel_cast(const void* x, int dt, int64_t rows, int64_t cols, int fmt, uint8_t* q, float* sinv,
                          hipStream_t st);
 void launch_group128_cast(const void* x, int dt, int64_t groups, int fmt, uint8_t* q, float* sinv, hipStream_t st);
