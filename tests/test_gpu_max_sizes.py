@@ -1,0 +1,128 @@
+"""GPU: the largest shapes, past every 32-bit boundary, checked against the
+CPU oracle on sampled elements (each sampled element's result depends only on
+its own group, tile or the tensor's amax, so the oracle computes it from the
+sampled inputs alone).  Inputs are generated on the device with seeded torch
+generators; only the samples travel to the host.
+
+- per-128-group cast and dequant of bf16 [300000, 7168] (2.15e9 elements, > 2^31)
+- per-tensor cast and dequant of 2^32 + 37 bf16 elements with the maximum
+  planted beyond 2^32
+- 128x128 block dequant of e4m3fn [4793491, 7168] (>= 2^32 lane vectors: the
+  row-strip kernel), 34 GB of codes and 69 GB of bf16 output
+"""
+import numpy as np
+import pytest
+import torch
+
+import dequantize_amax_reduce_amd as fq
+import oracle
+from gpu_util import assert_f32_equal, assert_fp8_equal, assert_hp_equal, host
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _gen(seed):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    return g
+
+
+def _bits(t):
+    return host(t)
+
+
+def _need(gib):
+    free, _ = torch.cuda.mem_get_info()
+    if free < gib * (1 << 30):
+        pytest.skip(f"needs {gib} GiB of free device memory, {free >> 30} GiB free")
+
+
+def _free(*ts):
+    del ts
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def test_group128_beyond_2_31_elements():
+    R, C = 300_000, 7168
+    _need(24)
+    print(f"[case] group128 [{R}, {C}] ({R * C} elements)", flush=True)
+    x = torch.randn((R, C), generator=_gen(81), device=DEV, dtype=torch.float32).to(torch.bfloat16)
+    q = torch.empty((R, C), dtype=torch.uint8, device=DEV)
+    s = torch.empty((R, C // 128), dtype=torch.float32, device=DEV)
+    y = torch.empty((R, C), dtype=torch.bfloat16, device=DEV)
+    fq.fp8q_cast_per_group128(x, q, s, "e4m3fn")
+    fq.fp8q_dequant_per_group128(q, s, y)
+    torch.cuda.synchronize()
+    rng = np.random.Generator(np.random.PCG64(82))
+    rows = np.unique(np.concatenate([[0, 1, R - 2, R - 1], rng.integers(0, R, 60),
+                                     rng.integers((1 << 31) // C, R, 8)]))
+    ri = torch.from_numpy(rows).to(DEV)
+    xs, qs, ss, ys = _bits(x[ri]), _bits(q[ri]), _bits(s[ri]), _bits(y[ri])
+    wq, ws = oracle.cast_per_group128(xs, "bf16", "e4m3fn")
+    assert_fp8_equal(qs, wq, "e4m3fn", "sampled rows q")
+    assert_f32_equal(ss, ws, "sampled rows scale_inv")
+    assert_hp_equal(ys, oracle.dequant_per_group128(wq, "e4m3fn", ws, "bf16"), "bf16", "sampled rows y")
+    _free(x, q, s, y)
+
+
+def test_per_tensor_beyond_2_32_elements():
+    n = (1 << 32) + 37
+    peak = (1 << 32) + 5
+    _need(32)
+    print(f"[case] per-tensor bf16 n={n}, maximum at {peak}", flush=True)
+    x = torch.randn(n, generator=_gen(83), device=DEV, dtype=torch.bfloat16)
+    x[peak] = -300.0                      # |x| of N(0, 1) stays far below 300 over 2^32 draws
+    q = torch.empty(n, dtype=torch.uint8, device=DEV)
+    si = torch.empty(1, dtype=torch.float32, device=DEV)
+    ws = torch.empty(fq.fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32, device=DEV)
+    amax = torch.empty(1, dtype=torch.float32, device=DEV)
+    fq.fp8q_amax(x, amax)
+    fq.fp8q_cast_per_tensor(x, q, si, ws, "e5m2")
+    torch.cuda.synchronize()
+    assert float(host(amax)[0]) == 300.0
+    rng = np.random.Generator(np.random.PCG64(84))
+    idx = np.unique(np.concatenate([[0, 1, peak, n - 37, n - 5, n - 1], rng.integers(0, n, 4000),
+                                    rng.integers(1 << 32, n, 30)]))
+    ti = torch.from_numpy(idx).to(DEV)
+    xs, qs = _bits(x[ti]), _bits(q[ti])
+    assert int(qs[np.nonzero(idx == peak)[0][0]]) == 0xFB          # -57344, the e5m2 maximum
+    # the oracle sees the sampled values, whose maximum is the planted one
+    wq, wsi = oracle.cast_per_tensor(xs, "bf16", "e5m2")
+    assert_f32_equal(host(si), wsi, "scale_inv")
+    assert_fp8_equal(qs, wq, "e5m2", "sampled q")
+    del x
+    torch.cuda.empty_cache()
+    y = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    fq.fp8q_dequant_per_tensor(q, si, y, "e5m2")
+    torch.cuda.synchronize()
+    assert_hp_equal(_bits(y[ti]), oracle.dequant_per_tensor(wq, "e5m2", wsi, "bf16"), "bf16", "sampled y")
+    _free(q, y, ws, amax, si)
+
+
+def test_block_dequant_row_strip_path():
+    M, N = 4_793_491, 7168                 # M * N / 8 >= 2^32 lane vectors; M % 128 = 19
+    assert M * N // 8 >= 1 << 32
+    _need(120)
+    print(f"[case] block dequant [{M}, {N}] ({M * N} codes)", flush=True)
+    c = torch.randint(0, 254, (M, N), generator=_gen(85), device=DEV, dtype=torch.uint8)
+    for r0 in range(0, M, 1 << 18):        # no NaN code (0x7F, 0xFF); bounded temporaries
+        blk = c[r0:r0 + (1 << 18)]
+        blk += (blk >= 0x7F).to(torch.uint8)
+    torch.cuda.empty_cache()
+    mb, nb = (M + 127) // 128, (N + 127) // 128
+    rng = np.random.Generator(np.random.PCG64(86))
+    sh = (10.0 ** rng.uniform(-4.0, -1.0, size=(mb, nb))).astype(np.float32)
+    s = torch.from_numpy(sh).to(DEV)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    fq.fp8q_weight_dequant_block128(c, s, y, "e4m3fn")
+    torch.cuda.synchronize()
+    ii = np.concatenate([[0, 0, M - 1, M - 1, M - 19, 127, 128], rng.integers(0, M, 3000)])
+    jj = np.concatenate([[0, N - 1, 0, N - 1, 4095, 127, 128], rng.integers(0, N, 3000)])
+    flat = torch.from_numpy(ii * N + jj).to(DEV)
+    cs = _bits(c.reshape(-1)[flat])
+    ys = _bits(y.reshape(-1)[flat])
+    want = oracle.dequant_per_channel(cs.reshape(-1, 1), "e4m3fn", sh[ii // 128, jj // 128], "bf16").reshape(-1)
+    assert_hp_equal(ys, want, "bf16", "sampled block dequant")
+    _free(c, s, y)
