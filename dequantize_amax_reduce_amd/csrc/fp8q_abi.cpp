@@ -87,6 +87,7 @@ const char* fp8q_status_str(int status) {
 }
 
 size_t fp8q_per_tensor_workspace_bytes(void) {
+    static_assert(fp8q::kAmaxPartials <= fp8q::kAmaxSlots * fp8q::kAmaxSlotStride, "partials must fit the workspace");
     return sizeof(uint32_t) * fp8q::kAmaxSlots * fp8q::kAmaxSlotStride;
 }
 
@@ -147,8 +148,8 @@ fp8q_status_t fp8q_cast_to_fp8_pipeline(const void* x, int xdtype, int64_t n, ui
     if (any_overlap(b, 5)) return FP8Q_EINVAL;
     // n == 0: the amax pass only clears the slots (amax 0); the cast launches
     // one workgroup that writes scale_inv and the format word
-    fp8q::launch_amax(x, xdtype, n, (uint32_t*)workspace, fp8q::kAmaxSlots, S(stream), true);
-    fp8q::launch_pipeline_cast(x, xdtype, n, (const uint32_t*)workspace, q, scale_inv, fmt_out, S(stream));
+    const int np = fp8q::launch_amax_partials(x, xdtype, n, (uint32_t*)workspace, S(stream));
+    fp8q::launch_pipeline_cast(x, xdtype, n, (const uint32_t*)workspace, np, q, scale_inv, fmt_out, S(stream));
     return launched();
 }
 
@@ -181,8 +182,8 @@ fp8q_status_t fp8q_cast_to_packed(const void* x, int xdtype, int64_t n, int fmt,
         fp8q::launch_fill_f32((float*)slot, 1, 1.0f, S(stream));
         return launched();
     }
-    fp8q::launch_amax(x, xdtype, n, (uint32_t*)workspace, fp8q::kAmaxSlots, S(stream), true);
-    fp8q::launch_tensor_cast(x, xdtype, n, fmt, (const uint32_t*)workspace, slot + 4, (float*)slot, S(stream));
+    const int np = fp8q::launch_amax_partials(x, xdtype, n, (uint32_t*)workspace, S(stream));
+    fp8q::launch_tensor_cast(x, xdtype, n, fmt, (const uint32_t*)workspace, np, slot + 4, (float*)slot, S(stream));
     return launched();
 }
 
@@ -217,8 +218,8 @@ fp8q_status_t fp8q_cast_per_tensor(const void* x, int xdtype, int64_t n, int fmt
         fp8q::launch_fill_f32(scale_inv, 1, 1.0f, S(stream));
         return launched();
     }
-    fp8q::launch_amax(x, xdtype, n, (uint32_t*)workspace, fp8q::kAmaxSlots, S(stream), true);
-    fp8q::launch_tensor_cast(x, xdtype, n, fmt, (const uint32_t*)workspace, q, scale_inv, S(stream));
+    const int np = fp8q::launch_amax_partials(x, xdtype, n, (uint32_t*)workspace, S(stream));
+    fp8q::launch_tensor_cast(x, xdtype, n, fmt, (const uint32_t*)workspace, np, q, scale_inv, S(stream));
     return launched();
 }
 
@@ -338,7 +339,7 @@ fp8q_status_t fp8q_dequant_sum_requant(const uint8_t* q, int fmt, int64_t W, int
         return launched();
     }
     fp8q::launch_dequant_sum(q, fmt, W, n, scale_inv, average, y, ydtype, (uint32_t*)workspace, S(stream));
-    fp8q::launch_tensor_cast(y, ydtype, n, fmt, (const uint32_t*)workspace, q_out, scale_inv_out, S(stream), true);
+    fp8q::launch_tensor_cast(y, ydtype, n, fmt, (const uint32_t*)workspace, 1, q_out, scale_inv_out, S(stream), true);
     return launched();
 }
 

@@ -422,9 +422,12 @@ __global__ void k_fill_f32(float* p, int64_t n, float v) {
 
 // VEC (x 16-B aligned): chunks of K sub-steps x 256 lane vectors per
 // workgroup trip; the n % VE tail element-wise by workgroup 0.
-// Stage 2 is an atomic max of each workgroup's result into one of `nslots`
-// amax slots (workgroup b uses slot b % nslots).
-template <int DT, bool VEC, int K, bool NT>
+// Stage 2: with PART, workgroup b stores its result to amax_bits[b] (one
+// partial per workgroup, every workgroup writes, so nothing needs clearing
+// and the consumer folds the partials); otherwise an atomic max of each
+// workgroup's result into one of `nslots` amax slots (workgroup b uses slot
+// b % nslots).
+template <int DT, bool VEC, int K, bool NT, bool PART = false>
 __global__ void __launch_bounds__(256)
 k_amax(const void* __restrict__ x, int64_t n, uint32_t* __restrict__ amax_bits, int nslots) {
     __shared__ uint32_t lds[4];
@@ -455,7 +458,19 @@ k_amax(const void* __restrict__ x, int64_t n, uint32_t* __restrict__ amax_bits, 
             m = umax(m, absbits1<DT>(x, i));
     }
     m = block_max256(m, lds);
-    if (threadIdx.x == 0 && m != 0) atomicMax(amax_bits + (blockIdx.x % nslots) * kAmaxSlotStride, m);
+    if constexpr (PART) {
+        if (threadIdx.x == 0) amax_bits[blockIdx.x] = m;
+    } else {
+        if (threadIdx.x == 0 && m != 0) atomicMax(amax_bits + (blockIdx.x % nslots) * kAmaxSlotStride, m);
+    }
+}
+
+// max over the np partials (binary32 bits of |x|); every thread of the
+// workgroup must call it (it contains barriers)
+__device__ __forceinline__ uint32_t fold_partials(const uint32_t* __restrict__ partial, int np, uint32_t* lds4) {
+    uint32_t a = 0;
+    for (int j = threadIdx.x; j < np; j += 256) a = umax(a, partial[j]);
+    return block_max256(a, lds4);
 }
 
 // scale from the finished amax: a = amax > 0 ? amax : 1 (NaN -> 1),
@@ -507,17 +522,70 @@ __device__ __forceinline__ void tensor_cast_body(const void* __restrict__ x, int
     }
 }
 
-// VEC: x 16-B aligned and q 4-byte aligned
+// The two-pass casts' second pass.  A workgroup first issues the loads of
+// its first chunk, then folds the amax partials (their latency hides behind
+// those loads), then scales and converts; with more chunks than workgroups
+// it loops over the rest.
+template <int DT, int K, bool NT>
+__device__ __forceinline__ void chunk_load(HpVec<DT>* v, const void* __restrict__ x, int64_t nvec, int64_t c) {
+    constexpr int VE = LaneVE<DT>::value;
+    constexpr int ESZ = ESize<DT>::value;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int64_t vi = (c * K + k) * 256 + threadIdx.x;
+        if (vi < nvec) v[k].template load<NT>((const char*)x + vi * VE * ESZ);
+    }
+}
+
+// cast the chunks of this workgroup (the first one already in v) and, in
+// workgroup 0, the n % VE tail
+template <int DT, int FMT, int K, bool NT, bool SAT>
+__device__ __forceinline__ void cast_chunks(HpVec<DT>* v, const void* __restrict__ x, int64_t n, float scale,
+                                            uint8_t* __restrict__ q) {
+    constexpr int VE = LaneVE<DT>::value;
+    const int64_t nvec = n / VE;
+    const int64_t nchunks = (nvec + K * 256 - 1) / (K * 256);
+    for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+        if (c != (int64_t)blockIdx.x) chunk_load<DT, K, NT>(v, x, nvec, c);
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int64_t vi = (c * K + k) * 256 + threadIdx.x;
+            if (vi < nvec) {
+                float f[VE];
+                v[k].widen(f);
+                scale_encode_store<FMT, SAT, VE, NT>(f, scale, q + vi * VE);
+            }
+        }
+    }
+    const int64_t i = nvec * VE + threadIdx.x;
+    if (blockIdx.x == 0 && i < n) {
+        float p = load1<DT>(x, i) * scale;
+        if constexpr (SAT) p = sat<FMT>(p);
+        q[i] = enc1<FMT>(p);
+    }
+}
+
+// VEC: x 16-B aligned and q 4-byte aligned.  The amax is the max of the np
+// partials (np = 1: an already folded amax).
 template <int DT, int FMT, bool VEC, int K, bool NT>
 __global__ void __launch_bounds__(256)
-k_tensor_cast(const void* __restrict__ x, int64_t n, const uint32_t* __restrict__ amax_bits,
+k_tensor_cast(const void* __restrict__ x, int64_t n, const uint32_t* __restrict__ partial, int np,
               uint8_t* __restrict__ q, float* __restrict__ sinv_out) {
-    const uint32_t ab = amax_bits[0];
+    __shared__ uint32_t lds[4];
+    HpVec<DT> v[K];
+    if constexpr (VEC) chunk_load<DT, K, NT>(v, x, n / LaneVE<DT>::value, blockIdx.x);
+    const uint32_t ab = fold_partials(partial, np, lds);
     float scale, sinv;
     tensor_scale<FMT>(ab, scale, sinv);
     if (blockIdx.x == 0 && threadIdx.x == 0) sinv_out[0] = sinv;
-    if (needs_saturation(ab, scale)) tensor_cast_body<DT, FMT, VEC, K, NT, true>(x, n, scale, q);  // uniform
-    else tensor_cast_body<DT, FMT, VEC, K, NT, false>(x, n, scale, q);
+    const bool saturate = needs_saturation(ab, scale);  // uniform
+    if constexpr (VEC) {
+        if (saturate) cast_chunks<DT, FMT, K, NT, true>(v, x, n, scale, q);
+        else cast_chunks<DT, FMT, K, NT, false>(v, x, n, scale, q);
+    } else {
+        if (saturate) tensor_cast_body<DT, FMT, false, K, NT, true>(x, n, scale, q);
+        else tensor_cast_body<DT, FMT, false, K, NT, false>(x, n, scale, q);
+    }
 }
 
 // Cast with a caller-supplied amax (ColossalAI fp8.py,
@@ -539,29 +607,40 @@ k_cast_given_amax(const void* __restrict__ x, int64_t n, const float* __restrict
 // e4m3fn maximum; a NaN amax fails the test) else e4m3fn; scale = 1 when
 // amax == 0, else that format's maximum / amax; scale_inv = 1 / scale.
 // Workgroup 0 publishes scale_inv and the format word (0 = e4m3fn,
-// 1 = e5m2).  Every workgroup takes the same decision from the same word, so
-// the branches are uniform.
+// 1 = e5m2).  Every workgroup takes the same decision from the same
+// partials, so the branches are uniform.
 template <int DT, int FMT, bool VEC, int K, bool NT>
-__device__ __forceinline__ void pipeline_cast_body(const void* __restrict__ x, int64_t n, uint32_t ab,
-                                                   uint8_t* __restrict__ q, float* __restrict__ sinv_out,
-                                                   int32_t* __restrict__ fmt_out) {
+__device__ __forceinline__ void pipeline_cast_rest(HpVec<DT>* v, const void* __restrict__ x, int64_t n,
+                                                   uint32_t ab, uint8_t* __restrict__ q,
+                                                   float* __restrict__ sinv_out, int32_t* __restrict__ fmt_out) {
     const float amax = __uint_as_float(ab);
     const float scale = (amax == 0.0f) ? 1.0f : Fp8Fmt<FMT>::max / amax;
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         sinv_out[0] = 1.0f / scale;
         fmt_out[0] = FMT;
     }
-    if (needs_saturation(ab, scale)) tensor_cast_body<DT, FMT, VEC, K, NT, true>(x, n, scale, q);
-    else tensor_cast_body<DT, FMT, VEC, K, NT, false>(x, n, scale, q);
+    const bool saturate = needs_saturation(ab, scale);
+    if constexpr (VEC) {
+        if (saturate) cast_chunks<DT, FMT, K, NT, true>(v, x, n, scale, q);
+        else cast_chunks<DT, FMT, K, NT, false>(v, x, n, scale, q);
+    } else {
+        if (saturate) tensor_cast_body<DT, FMT, false, K, NT, true>(x, n, scale, q);
+        else tensor_cast_body<DT, FMT, false, K, NT, false>(x, n, scale, q);
+    }
 }
 
 template <int DT, bool VEC, int K, bool NT>
 __global__ void __launch_bounds__(256)
-k_pipeline_cast(const void* __restrict__ x, int64_t n, const uint32_t* __restrict__ amax_bits,
+k_pipeline_cast(const void* __restrict__ x, int64_t n, const uint32_t* __restrict__ partial, int np,
                 uint8_t* __restrict__ q, float* __restrict__ sinv_out, int32_t* __restrict__ fmt_out) {
-    const uint32_t ab = amax_bits[0];
-    if (__uint_as_float(ab) > Fp8Fmt<kE4M3>::max) pipeline_cast_body<DT, kE5M2, VEC, K, NT>(x, n, ab, q, sinv_out, fmt_out);
-    else pipeline_cast_body<DT, kE4M3, VEC, K, NT>(x, n, ab, q, sinv_out, fmt_out);
+    __shared__ uint32_t lds[4];
+    HpVec<DT> v[K];
+    if constexpr (VEC) chunk_load<DT, K, NT>(v, x, n / LaneVE<DT>::value, blockIdx.x);
+    const uint32_t ab = fold_partials(partial, np, lds);
+    if (__uint_as_float(ab) > Fp8Fmt<kE4M3>::max)
+        pipeline_cast_rest<DT, kE5M2, VEC, K, NT>(v, x, n, ab, q, sinv_out, fmt_out);
+    else
+        pipeline_cast_rest<DT, kE4M3, VEC, K, NT>(v, x, n, ab, q, sinv_out, fmt_out);
 }
 
 // ===========================================================================

@@ -21,7 +21,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int64_t kGridCap = 1 << 20;   // grid-stride beyond this many workgroups
-constexpr int64_t kAmaxGrid = 1024;
+constexpr int64_t kAmaxGrid = kAmaxPartials;  // amax-pass workgroups (and partials)
 constexpr int64_t kSumAmaxGrid = 8192;  // the reduce step's sum pass when it also folds the amax
 
 constexpr int kGroupK = 2;        // sub-steps per group-cast chunk
@@ -75,14 +75,15 @@ template <int DT, int FMT> struct RunGroup128 {
 // cast pass whose input was just written by the previous kernel (the
 // reduce step's re-cast: 90.4 us against 93.1 us for 8 x 2^25 e5m2 chunks)
 template <int DT, int FMT> struct RunTensorCast {
-    static void run(const void* x, int64_t n, const uint32_t* ws, uint8_t* q, float* sinv, bool cached,
+    static void run(const void* x, int64_t n, const uint32_t* partial, int np, uint8_t* q, float* sinv, bool cached,
                     hipStream_t st) {
         constexpr int VE = LaneVE<DT>::value;
         const bool vec = al(x, 16) && al(q, 4);
         const unsigned nb = vec ? grid((n / VE + kFlatK * 256 - 1) / (kFlatK * 256)) : grid((n + 255) / 256);
-        if (vec && cached) k_tensor_cast<DT, FMT, true, kFlatK, false><<<nb, kThreads, 0, st>>>(x, n, ws, q, sinv);
-        else if (vec) k_tensor_cast<DT, FMT, true, kFlatK, kNT><<<nb, kThreads, 0, st>>>(x, n, ws, q, sinv);
-        else k_tensor_cast<DT, FMT, false, kFlatK, kNT><<<nb, kThreads, 0, st>>>(x, n, ws, q, sinv);
+        if (vec && cached)
+            k_tensor_cast<DT, FMT, true, kFlatK, false><<<nb, kThreads, 0, st>>>(x, n, partial, np, q, sinv);
+        else if (vec) k_tensor_cast<DT, FMT, true, kFlatK, kNT><<<nb, kThreads, 0, st>>>(x, n, partial, np, q, sinv);
+        else k_tensor_cast<DT, FMT, false, kFlatK, kNT><<<nb, kThreads, 0, st>>>(x, n, partial, np, q, sinv);
     }
 };
 
@@ -113,30 +114,47 @@ template <int DT, int FMT> struct RunChannel {
     }
 };
 
-// The amax grid is capped at kAmaxGrid workgroups looping over chunks: one
-// atomic per workgroup, spread over the slots (measured on the gradient
-// workload: 83 us with 64 line-separated slots, 87 us with one word, and
-// 758 us with one word and one chunk per workgroup).  `cached`: ordinary
-// loads instead of non-temporal ones, for an amax pass that a cast pass over
-// the same x follows -- what the amax pass leaves in L2 and the Infinity
-// Cache the cast pass gets for free (per-tensor cast, bf16 [4096, 4096]:
-// 20.5 us against 26.9 us; 2^28 elements: 210.9 against 212.9 us).  A
-// stand-alone amax keeps non-temporal loads (2^28: 85 against 91 us).
-template <int DT> void run_amax(const void* x, int64_t n, uint32_t* ws, int nslots, bool cached, hipStream_t st) {
+// The stand-alone amax (fp8q_amax): its grid is capped at kAmaxGrid
+// workgroups looping over chunks, each ending in one atomic max into the
+// slots (measured on the gradient workload: 83 us with 64 line-separated
+// slots, 87 us with one word, and 758 us with one word and one chunk per
+// workgroup).  Non-temporal loads: nothing re-reads x.
+template <int DT> void run_amax(const void* x, int64_t n, uint32_t* ws, int nslots, hipStream_t st) {
     k_fill_slots<<<1, 64, 0, st>>>(ws, nslots, 0u);
     if (n == 0) return;
     constexpr int VE = LaneVE<DT>::value;
     const int64_t cap = kAmaxGrid;
     if (al(x, 16)) {
         const int64_t chunks = (n / VE + kAmaxK * 256 - 1) / (kAmaxK * 256);
-        const unsigned nb = (unsigned)std::min(std::max<int64_t>(chunks, 1), cap);
-        if (cached) k_amax<DT, true, kAmaxK, false><<<nb, kThreads, 0, st>>>(x, n, ws, nslots);
-        else k_amax<DT, true, kAmaxK, kNT><<<nb, kThreads, 0, st>>>(x, n, ws, nslots);
+        k_amax<DT, true, kAmaxK, kNT><<<(unsigned)std::min(std::max<int64_t>(chunks, 1), cap), kThreads, 0, st>>>(
+            x, n, ws, nslots);
     } else {
         k_amax<DT, false, kAmaxK, false><<<(unsigned)std::min((n + 255) / 256, cap), kThreads, 0, st>>>(x, n, ws,
                                                                                                        nslots);
     }
     if (nslots > 1) k_fold_slots<<<1, 64, 0, st>>>(ws, nslots);
+}
+
+// The amax pass of a two-pass cast: at most kAmaxGrid workgroups, each
+// storing one partial (no clearing, no atomics, no fold launch: the cast
+// pass folds the partials itself).  Returns the number of partials.
+// Ordinary (cached) loads: the cast pass re-reads x, and what this pass
+// leaves in L2 and the Infinity Cache it gets for free (per-tensor cast,
+// bf16 [4096, 4096]: 20.5 us against 26.9 us with non-temporal loads).
+// Two launches instead of four (slot clear, atomics, slot fold): the bf16
+// [4096, 4096] cast takes 16.4 us against 20.8 us, fp32 28.5 against 31.9.
+template <int DT> int run_amax_partials(const void* x, int64_t n, uint32_t* partial, hipStream_t st) {
+    constexpr int VE = LaneVE<DT>::value;
+    const int64_t cap = kAmaxGrid;
+    if (al(x, 16)) {
+        const int64_t chunks = (n / VE + kAmaxK * 256 - 1) / (kAmaxK * 256);
+        const int g = (int)std::min(std::max<int64_t>(chunks, 1), cap);
+        k_amax<DT, true, kAmaxK, false, true><<<g, kThreads, 0, st>>>(x, n, partial, 0);
+        return g;
+    }
+    const int g = (int)std::min(std::max<int64_t>((n + 255) / 256, 1), cap);
+    k_amax<DT, false, kAmaxK, false, true><<<g, kThreads, 0, st>>>(x, n, partial, 0);
+    return g;
 }
 
 template <int FMT, int YDT> struct RunDequantFlat {
@@ -157,15 +175,16 @@ template <int FMT, int YDT> struct RunDequantFlat {
     }
 };
 
-template <int DT> void run_pipeline_cast(const void* x, int64_t n, const uint32_t* ws, uint8_t* q, float* sinv,
-                                         int32_t* fmt_out, hipStream_t st) {
+template <int DT> void run_pipeline_cast(const void* x, int64_t n, const uint32_t* partial, int np, uint8_t* q,
+                                         float* sinv, int32_t* fmt_out, hipStream_t st) {
     constexpr int VE = LaneVE<DT>::value;
     if (al(x, 16) && al(q, 4)) {
         const int64_t chunks = (n / VE + kFlatK * 256 - 1) / (kFlatK * 256);
-        k_pipeline_cast<DT, true, kFlatK, kNT><<<grid(chunks), kThreads, 0, st>>>(x, n, ws, q, sinv, fmt_out);
+        k_pipeline_cast<DT, true, kFlatK, kNT><<<grid(chunks), kThreads, 0, st>>>(x, n, partial, np, q, sinv,
+                                                                                  fmt_out);
     } else {
-        k_pipeline_cast<DT, false, kFlatK, kNT><<<grid((n + 255) / 256), kThreads, 0, st>>>(x, n, ws, q, sinv,
-                                                                                             fmt_out);
+        k_pipeline_cast<DT, false, kFlatK, kNT><<<grid((n + 255) / 256), kThreads, 0, st>>>(x, n, partial, np, q,
+                                                                                             sinv, fmt_out);
     }
 }
 
@@ -257,15 +276,21 @@ void launch_fill_f32(float* p, int64_t n, float v, hipStream_t st) {
     k_fill_f32<<<grid((n + kThreads - 1) / kThreads), kThreads, 0, st>>>(p, n, v);
 }
 
-void launch_amax(const void* x, int dt, int64_t n, uint32_t* ws, int nslots, hipStream_t st, bool cached) {
-    if (dt == kF32) run_amax<kF32>(x, n, ws, nslots, cached, st);
-    else if (dt == kBF16) run_amax<kBF16>(x, n, ws, nslots, cached, st);
-    else run_amax<kF16>(x, n, ws, nslots, cached, st);
+void launch_amax(const void* x, int dt, int64_t n, uint32_t* ws, int nslots, hipStream_t st) {
+    if (dt == kF32) run_amax<kF32>(x, n, ws, nslots, st);
+    else if (dt == kBF16) run_amax<kBF16>(x, n, ws, nslots, st);
+    else run_amax<kF16>(x, n, ws, nslots, st);
 }
 
-void launch_tensor_cast(const void* x, int dt, int64_t n, int fmt, const uint32_t* ws, uint8_t* q, float* sinv,
-                        hipStream_t st, bool cached) {
-    dispatch_dt_fmt<RunTensorCast>(dt, fmt, x, n, ws, q, sinv, cached, st);
+int launch_amax_partials(const void* x, int dt, int64_t n, uint32_t* partial, hipStream_t st) {
+    if (dt == kF32) return run_amax_partials<kF32>(x, n, partial, st);
+    if (dt == kBF16) return run_amax_partials<kBF16>(x, n, partial, st);
+    return run_amax_partials<kF16>(x, n, partial, st);
+}
+
+void launch_tensor_cast(const void* x, int dt, int64_t n, int fmt, const uint32_t* partial, int np, uint8_t* q,
+                        float* sinv, hipStream_t st, bool cached) {
+    dispatch_dt_fmt<RunTensorCast>(dt, fmt, x, n, partial, np, q, sinv, cached, st);
 }
 
 void launch_guard_amax(uint32_t* ws, hipStream_t st) { k_guard_amax<<<1, 64, 0, st>>>(ws); }
@@ -275,11 +300,11 @@ void launch_cast_given_amax(const void* x, int dt, int64_t n, int fmt, const flo
     dispatch_dt_fmt<RunCastGivenAmax>(dt, fmt, x, n, amax, q, scale_out, st);
 }
 
-void launch_pipeline_cast(const void* x, int dt, int64_t n, const uint32_t* ws, uint8_t* q, float* sinv,
-                          int32_t* fmt_out, hipStream_t st) {
-    if (dt == kF32) run_pipeline_cast<kF32>(x, n, ws, q, sinv, fmt_out, st);
-    else if (dt == kBF16) run_pipeline_cast<kBF16>(x, n, ws, q, sinv, fmt_out, st);
-    else run_pipeline_cast<kF16>(x, n, ws, q, sinv, fmt_out, st);
+void launch_pipeline_cast(const void* x, int dt, int64_t n, const uint32_t* partial, int np, uint8_t* q,
+                          float* sinv, int32_t* fmt_out, hipStream_t st) {
+    if (dt == kF32) run_pipeline_cast<kF32>(x, n, partial, np, q, sinv, fmt_out, st);
+    else if (dt == kBF16) run_pipeline_cast<kBF16>(x, n, partial, np, q, sinv, fmt_out, st);
+    else run_pipeline_cast<kF16>(x, n, partial, np, q, sinv, fmt_out, st);
 }
 
 void launch_dequant_pipeline(const uint8_t* q, int64_t n, const float* sinv, const int32_t* fmt, void* y, int ydt,

@@ -14,15 +14,20 @@ enum { kE4M3 = 0, kE5M2 = 1 };
 // (checked by the ABI layer): sizes > 0 unless stated, pointers valid and
 // aligned to their element size, buffers non-overlapping.
 void launch_fill_f32(float* p, int64_t n, float v, hipStream_t st);
-// Per-tensor amax slots: the workspace of the per-tensor cast holds
-// kAmaxSlots words, kAmaxSlotStride words (128 bytes) apart; the finished
-// amax is their max.
+// Amax slots (the stand-alone amax and the reduce step's re-cast): kAmaxSlots
+// words, kAmaxSlotStride words (128 bytes) apart; the finished amax is their
+// max, folded into slot 0.
 constexpr int kAmaxSlots = 64;
 constexpr int kAmaxSlotStride = 32;
+// Amax partials (the two-pass casts): at most kAmaxPartials words, one per
+// workgroup of the amax pass; the cast pass folds them.
+constexpr int kAmaxPartials = 1024;
 // clears the nslots amax slots of ws, folds max |x| (binary32 bits) into them and
-// leaves the result in ws[0]; n may be 0.  cached: x is read through the
-// caches because a cast pass over the same x follows.
-void launch_amax(const void* x, int dt, int64_t n, uint32_t* ws, int nslots, hipStream_t st, bool cached = false);
+// leaves the result in ws[0]; n may be 0
+void launch_amax(const void* x, int dt, int64_t n, uint32_t* ws, int nslots, hipStream_t st);
+// the amax pass of a two-pass cast: stores one partial max |x| per workgroup
+// to partial[0 .. np) and returns np (1 <= np <= kAmaxPartials); n may be 0
+int launch_amax_partials(const void* x, int dt, int64_t n, uint32_t* partial, hipStream_t st);
 // where(amax > 0, amax, 1) applied to ws[0]
 void launch_guard_amax(uint32_t* ws, hipStream_t st);
 // cast with scale = fp8_max / amax[0] (caller-supplied amax); scale_out[0] = scale
@@ -30,17 +35,18 @@ void launch_cast_given_amax(const void* x, int dt, int64_t n, int fmt, const flo
                             float* scale_out, hipStream_t st);
 // dequant of W packed [scale_inv | n codes] slots into y [W][n]
 void launch_dequant_packed(const uint8_t* slots, int fmt, int64_t W, int64_t n, void* y, int ydt, hipStream_t st);
-// pipeline cast with amax = ws[0]: the format chosen on the device, written to fmt_out[0]
-void launch_pipeline_cast(const void* x, int dt, int64_t n, const uint32_t* ws, uint8_t* q, float* sinv,
-                          int32_t* fmt_out, hipStream_t st);
+// pipeline cast with amax = max of partial[0 .. np): the format chosen on the
+// device, written to fmt_out[0]
+void launch_pipeline_cast(const void* x, int dt, int64_t n, const uint32_t* partial, int np, uint8_t* q,
+                          float* sinv, int32_t* fmt_out, hipStream_t st);
 // per-tensor dequant with the format read from fmt[0] on the device
 void launch_dequant_pipeline(const uint8_t* q, int64_t n, const float* sinv, const int32_t* fmt, void* y, int ydt,
                              hipStream_t st);
-// the scale-and-cast pass, with amax = ws[0]
-// (cached: ordinary instead of non-temporal memory accesses, for an input
-// the previous kernel just wrote)
-void launch_tensor_cast(const void* x, int dt, int64_t n, int fmt, const uint32_t* ws, uint8_t* q, float* sinv,
-                        hipStream_t st, bool cached = false);
+// the scale-and-cast pass, with amax = max of partial[0 .. np) (np = 1: an
+// already folded amax).  cached: ordinary instead of non-temporal memory
+// accesses, for an input the previous kernel just wrote.
+void launch_tensor_cast(const void* x, int dt, int64_t n, int fmt, const uint32_t* partial, int np, uint8_t* q,
+                        float* sinv, hipStream_t st, bool cached = false);
 void launch_channel_cast(const void* x, int dt, int64_t rows, int64_t cols, int fmt, uint8_t* q, float* sinv,
                          hipStream_t st);
 void launch_group128_cast(const void* x, int dt, int64_t groups, int fmt, uint8_t* q, float* sinv, hipStream_t st);
