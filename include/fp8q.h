@@ -68,10 +68,11 @@ int fp8q_abi_version(void);
 /* static, human-readable name of a status code (never NULL) */
 const char* fp8q_status_str(int status);
 
-/* bytes of device workspace fp8q_cast_per_tensor and fp8q_dequant_sum_requant
- * need (8192): 64 binary32 amax slots, one per 128-byte line; the stage-1
- * workgroups fold their maxima into slot (workgroup % 64), so the atomics do
- * not serialise on one cache line */
+/* bytes of device workspace (8192) that fp8q_cast_per_tensor,
+ * fp8q_cast_to_fp8_pipeline, fp8q_cast_to_packed and fp8q_dequant_sum_requant
+ * need.  Its contents are the library's scratch between the passes of one
+ * call (amax partials or amax slots); it needs no initialisation and holds
+ * nothing the caller reads. */
 size_t fp8q_per_tensor_workspace_bytes(void);
 
 /*
