@@ -94,8 +94,8 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
-              "(the row/group/block kernels shard by rows with no exchange; see the design notes)",
+        print(f"bench.py: fp8q measures one GPU only; --gpus {args.gpus} is not supported (the row, group and "
+              "block kernels would shard by rows with no exchange, so a multi-GPU run is N independent copies)",
               file=sys.stderr)
         sys.exit(2)
 
@@ -262,12 +262,13 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def measured_traffic():
+def measured_traffic(path=None):
     """HBM bytes per launch of the group-cast kernel from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None when that summary is
     missing or was taken on different kernel sources."""
     import re
-    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), TRAFFIC_SUMMARY)
+    if path is None:
+        path = os.path.join(os.path.dirname(os.path.abspath(__file__)), TRAFFIC_SUMMARY)
     try:
         text = open(path).read()
     except OSError:
