@@ -29,10 +29,19 @@ def _run_all(b):
         fq.fp8q_cast_to_packed(b["x"].reshape(-1)[r * n:(r + 1) * n], b["pk"][r * (4 + n):(r + 1) * (4 + n)],
                                b["ws"], "e5m2")
     fq.fp8q_dequant_packed(b["pk"], 2, n, b["ypk"], "e5m2")
+    # reduce step (slot clear, atomics and fold inside the graph) and the FSDP hook's parts
+    fq.fp8q_dequant_sum(b["pk_codes"], b["pk_sinv"], b["ysum"], "e5m2", True)
+    fq.fp8q_dequant_sum_requant(b["pk_codes"], b["pk_sinv"], b["yrq"], b["qrq"], b["srq"], b["ws2"], "e5m2", False)
+    fq.fp8q_amax_guarded(b["x"], b["amg"])
+    fq.fp8q_cast_with_amax(b["x"], b["amg"], b["qfs"], b["sfs"], "e5m2")
+    fq.fp8q_dequant_div_scale(b["qfs"], b["sfs"], b["yfs"], "e5m2")
+
+
+INPUTS = ("x", "qw", "sw", "pk_codes", "pk_sinv")
 
 
 def _outputs(b):
-    return {k: host(v).copy() for k, v in b.items() if k not in ("x", "qw", "sw", "ws")}
+    return {k: host(v).copy() for k, v in b.items() if k not in INPUTS + ("ws", "ws2")}
 
 
 def test_graph_replays_match_eager():
@@ -61,6 +70,17 @@ def test_graph_replays_match_eager():
         "yp": torch.empty((R, C), dtype=torch.bfloat16, device=dev),
         "pk": torch.empty(2 * (4 + R * C // 2), dtype=torch.uint8, device=dev),
         "ypk": torch.empty((R, C), dtype=torch.bfloat16, device=dev),
+        "pk_codes": torch.from_numpy(W.received_chunks(4, R * C // 4, "e5m2", seed=9)[0]).to(dev),
+        "pk_sinv": torch.from_numpy(W.received_chunks(4, R * C // 4, "e5m2", seed=9)[1]).to(dev),
+        "ysum": torch.empty(R * C // 4, dtype=torch.bfloat16, device=dev),
+        "yrq": torch.empty(R * C // 4, dtype=torch.bfloat16, device=dev),
+        "qrq": torch.empty(R * C // 4, dtype=torch.uint8, device=dev),
+        "srq": torch.empty(1, dtype=torch.float32, device=dev),
+        "ws2": torch.empty(fq.fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32, device=dev),
+        "amg": torch.empty(1, dtype=torch.float32, device=dev),
+        "qfs": torch.empty((R, C), dtype=torch.uint8, device=dev),
+        "sfs": torch.empty(1, dtype=torch.float32, device=dev),
+        "yfs": torch.empty((R, C), dtype=torch.bfloat16, device=dev),
     }
     _run_all(b)                       # eager reference (also warms up every kernel)
     torch.cuda.synchronize()
@@ -76,7 +96,7 @@ def test_graph_replays_match_eager():
 
     for rep in range(4):
         for k, v in b.items():       # eager work between replays: scribble over every output
-            if k not in ("x", "qw", "sw"):
+            if k not in INPUTS:
                 v.view(torch.uint8).fill_(0xA5)
         torch.cuda.synchronize()
         print(f"[case] graph replay {rep}", flush=True)
