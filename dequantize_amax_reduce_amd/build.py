@@ -51,7 +51,28 @@ def build(verbose: bool = False) -> str:
     if msgs.strip() and verbose:
         print(msgs)
     os.replace(tmp, LIB)
+    build_example(verbose)
     return LIB
+
+
+EXAMPLE_SRC = os.path.join(PKG, "examples", "c_abi_example.c")
+EXAMPLE = os.path.join(PKG, "fp8q_c_example")
+
+
+def build_example(verbose: bool = False) -> str:
+    """A plain C program that calls the library through include/fp8q.h and
+    the HIP runtime API only (no torch, no C++), linked next to libfp8q.so."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    cmd = [os.environ.get("CC", "gcc"), "-std=c11", "-O2", "-Wall", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(rocm, "include"), "-I", INCLUDE, EXAMPLE_SRC, "-o", EXAMPLE,
+           "-L", PKG, "-lfp8q", "-L", os.path.join(rocm, "lib"), "-lamdhip64", "-lm",
+           "-Wl,-rpath,$ORIGIN", "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"building the C example failed ({r.returncode}):\n{r.stdout}{r.stderr}")
+    return EXAMPLE
 
 
 if __name__ == "__main__":
