@@ -720,6 +720,54 @@ k_channel_2pass(const void* __restrict__ x, int64_t rows, int64_t cols, uint8_t*
     }
 }
 
+// Long rows with the vector layout (cols % VE == 0, x 16-B aligned, q 4-byte
+// aligned, cols > 2048 * VE): pass 1 reduces the row with ordinary (cached)
+// 16-byte loads, U lane vectors per thread in flight; pass 2 re-reads it,
+// mostly from L2 and the Infinity Cache, and casts.
+template <int DT, int FMT, int U, bool NT>
+__global__ void __launch_bounds__(256)
+k_channel_2pass_vec(const void* __restrict__ x, int64_t rows, int64_t cols, uint8_t* __restrict__ q,
+                    float* __restrict__ sinv_out) {
+    __shared__ uint32_t lds[4];
+    constexpr int VE = LaneVE<DT>::value;
+    constexpr int ESZ = ESize<DT>::value;
+    const int64_t nvec = cols / VE;
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+        const char* xr = (const char*)x + r * cols * ESZ;
+        uint32_t m = 0;
+        for (int64_t v0 = threadIdx.x; v0 < nvec; v0 += U * 256) {
+            HpVec<DT> v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (v0 + u * 256 < nvec) v[u].template load<false>(xr + (v0 + u * 256) * VE * ESZ);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (v0 + u * 256 < nvec) m = umax(m, v[u].absmax_bits());
+        }
+        m = block_max256(m, lds);
+        float scale, sinv;
+        channel_scale<FMT>(m, scale, sinv);
+        if (threadIdx.x == 0) sinv_out[r] = sinv;
+        const bool saturate = needs_saturation(m, scale);
+        for (int64_t v0 = threadIdx.x; v0 < nvec; v0 += U * 256) {
+            HpVec<DT> v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (v0 + u * 256 < nvec) v[u].template load<NT>(xr + (v0 + u * 256) * VE * ESZ);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t vi = v0 + u * 256;
+                if (vi < nvec) {
+                    float f[VE];
+                    v[u].widen(f);
+                    if (saturate) scale_encode_store<FMT, true, VE, NT>(f, scale, q + r * cols + vi * VE);
+                    else scale_encode_store<FMT, false, VE, NT>(f, scale, q + r * cols + vi * VE);
+                }
+            }
+        }
+    }
+}
+
 // ===========================================================================
 // dequant (ColossalAI fp8.py cast_from_fp8; inverse of per_token_cast_to_fp8)
 // ===========================================================================

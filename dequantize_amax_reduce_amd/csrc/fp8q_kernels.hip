@@ -110,6 +110,9 @@ template <int DT, int FMT> struct RunChannel {
         else if (vec && nvec <= 512) k_channel_reg<DT, FMT, 2, kNT><<<nb, kThreads, 0, st>>>(x, rows, cols, q, sinv);
         else if (vec && nvec <= 1024) k_channel_reg<DT, FMT, 4, kNT><<<nb, kThreads, 0, st>>>(x, rows, cols, q, sinv);
         else if (vec && nvec <= 2048) k_channel_reg<DT, FMT, 8, kNT><<<nb, kThreads, 0, st>>>(x, rows, cols, q, sinv);
+        // longer rows: two vector passes over the row (fp32 [256, 131072]: 46 us
+        // against 347 us element-wise; bf16 [4000, 16400]: 44 against 120 us)
+        else if (vec) k_channel_2pass_vec<DT, FMT, 8, kNT><<<nb, kThreads, 0, st>>>(x, rows, cols, q, sinv);
         else k_channel_2pass<DT, FMT><<<nb, kThreads, 0, st>>>(x, rows, cols, q, sinv);
     }
 };

@@ -91,7 +91,7 @@ def test_tensor_channel_config_full_size(dtype, fmt):
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("rows,cols", [(1, 1), (3, 15), (7, 16), (33, 4096), (5, 4112), (4, 8192),
-                                       (3, 16384), (2, 16400), (2, 40000)])
+                                       (3, 16384), (2, 16400), (2, 40000), (2, 40001), (37, 65536)])
 def test_channel_shapes(rows, cols, fmt, dtype):
     x = _rows_scaled(rows, cols, seed=rows + cols)["f32"]
     if dtype == "bf16":
