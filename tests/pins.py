@@ -764,4 +764,8 @@ def pin_packed_layout_closed_form(L):
         assert y.tolist() == [[fmax, -1.0], [2 * fmax, -2.0]], (fmt, y)
 
 
-ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
+# the exact-rational cast references are the slow ones (seconds each): run last,
+# so that a planted mistake caught by a cheaper pin is reported sooner
+_SLOW = ("pin_exact_cast_per_group128", "pin_exact_cast_per_tensor", "pin_exact_cast_per_channel")
+ALL_PINS = ([v for k, v in sorted(globals().items()) if k.startswith("pin_") and k not in _SLOW]
+            + [globals()[k] for k in _SLOW])
