@@ -98,7 +98,7 @@ fp8q_status_t fp8q_amax(const void* x, int xdtype, int64_t n, float* amax, void*
     if (!amax || (n > 0 && !x)) return FP8Q_EINVAL;
     if (!aligned(amax, 4) || (x && !aligned(x, esize(xdtype)))) return FP8Q_EALIGN;
     if (overlap(x, xbytes, amax, 4)) return FP8Q_EINVAL;
-    fp8q::launch_amax(x, xdtype, n, (uint32_t*)amax, 1, S(stream));
+    fp8q::launch_amax(x, xdtype, n, (uint32_t*)amax, S(stream));
     return launched();
 }
 
@@ -303,9 +303,10 @@ fp8q_status_t fp8q_weight_dequant_block128(const uint8_t* q, int fmt, int64_t M,
 
 // shared validation of the reduce-step entry points
 static fp8q_status_t check_sum(const uint8_t* q, int fmt, int64_t W, int64_t n, const float* scale_inv, const void* y,
-                               int ydtype, int64_t* qbytes, int64_t* ybytes) {
+                               int ydtype, int64_t* qbytes, int64_t* ybytes, int64_t* sbytes) {
     if (!valid_dtype(ydtype) || !valid_fmt(fmt)) return FP8Q_EDTYPE;
-    if (W < 1 || n < 0 || !mul_ok(W, n, qbytes) || !mul_ok(n, esize(ydtype), ybytes)) return FP8Q_EINVAL;
+    if (W < 1 || n < 0 || !mul_ok(W, n, qbytes) || !mul_ok(n, esize(ydtype), ybytes) || !mul_ok(W, 4, sbytes))
+        return FP8Q_EINVAL;
     if (!scale_inv || (n > 0 && (!q || !y))) return FP8Q_EINVAL;
     if (!aligned(scale_inv, 4) || (y && !aligned(y, esize(ydtype)))) return FP8Q_EALIGN;
     return FP8Q_OK;
@@ -313,10 +314,10 @@ static fp8q_status_t check_sum(const uint8_t* q, int fmt, int64_t W, int64_t n, 
 
 fp8q_status_t fp8q_dequant_sum(const uint8_t* q, int fmt, int64_t W, int64_t n, const float* scale_inv, int average,
                                void* y, int ydtype, void* stream) {
-    int64_t qbytes, ybytes;
-    fp8q_status_t st = check_sum(q, fmt, W, n, scale_inv, y, ydtype, &qbytes, &ybytes);
+    int64_t qbytes, ybytes, sbytes;
+    fp8q_status_t st = check_sum(q, fmt, W, n, scale_inv, y, ydtype, &qbytes, &ybytes, &sbytes);
     if (st != FP8Q_OK) return st;
-    const Buf b[3] = {{q, qbytes}, {scale_inv, W * 4}, {y, ybytes}};
+    const Buf b[3] = {{q, qbytes}, {scale_inv, sbytes}, {y, ybytes}};
     if (any_overlap(b, 3)) return FP8Q_EINVAL;
     if (n == 0) return FP8Q_OK;
     fp8q::launch_dequant_sum(q, fmt, W, n, scale_inv, average, y, ydtype, nullptr, S(stream));
@@ -326,13 +327,13 @@ fp8q_status_t fp8q_dequant_sum(const uint8_t* q, int fmt, int64_t W, int64_t n, 
 fp8q_status_t fp8q_dequant_sum_requant(const uint8_t* q, int fmt, int64_t W, int64_t n, const float* scale_inv,
                                        int average, void* y, int ydtype, uint8_t* q_out, float* scale_inv_out,
                                        void* workspace, void* stream) {
-    int64_t qbytes, ybytes;
-    fp8q_status_t st = check_sum(q, fmt, W, n, scale_inv, y, ydtype, &qbytes, &ybytes);
+    int64_t qbytes, ybytes, sbytes;
+    fp8q_status_t st = check_sum(q, fmt, W, n, scale_inv, y, ydtype, &qbytes, &ybytes, &sbytes);
     if (st != FP8Q_OK) return st;
     if (!scale_inv_out || !workspace || (n > 0 && !q_out)) return FP8Q_EINVAL;
     if (!aligned(scale_inv_out, 4) || !aligned(workspace, 4)) return FP8Q_EALIGN;
     const int64_t wsb = (int64_t)fp8q_per_tensor_workspace_bytes();
-    const Buf b[6] = {{q, qbytes}, {scale_inv, W * 4}, {y, ybytes}, {q_out, n}, {scale_inv_out, 4}, {workspace, wsb}};
+    const Buf b[6] = {{q, qbytes}, {scale_inv, sbytes}, {y, ybytes}, {q_out, n}, {scale_inv_out, 4}, {workspace, wsb}};
     if (any_overlap(b, 6)) return FP8Q_EINVAL;
     if (n == 0) {
         fp8q::launch_fill_f32(scale_inv_out, 1, 1.0f, S(stream));

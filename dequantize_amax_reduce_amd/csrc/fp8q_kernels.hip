@@ -117,25 +117,25 @@ template <int DT, int FMT> struct RunChannel {
     }
 };
 
-// The stand-alone amax (fp8q_amax): its grid is capped at kAmaxGrid
-// workgroups looping over chunks, each ending in one atomic max into the
-// slots (measured on the gradient workload: 83 us with 64 line-separated
-// slots, 87 us with one word, and 758 us with one word and one chunk per
-// workgroup).  Non-temporal loads: nothing re-reads x.
-template <int DT> void run_amax(const void* x, int64_t n, uint32_t* ws, int nslots, hipStream_t st) {
-    k_fill_slots<<<1, 64, 0, st>>>(ws, nslots, 0u);
+// The stand-alone amax (fp8q_amax, into one caller word): its grid is capped
+// at kAmaxGrid workgroups looping over chunks, each ending in one atomic max
+// on the word (measured on the gradient workload: 87 us with one word against
+// 758 us with one chunk per workgroup, where the atomics serialise; 64 slots
+// on separate lines would give 83 us but need a workspace).  Non-temporal
+// loads: nothing re-reads x.
+template <int DT> void run_amax(const void* x, int64_t n, uint32_t* word, hipStream_t st) {
+    k_fill_slots<<<1, 64, 0, st>>>(word, 1, 0u);
     if (n == 0) return;
     constexpr int VE = LaneVE<DT>::value;
     const int64_t cap = kAmaxGrid;
     if (al(x, 16)) {
         const int64_t chunks = (n / VE + kAmaxK * 256 - 1) / (kAmaxK * 256);
         k_amax<DT, true, kAmaxK, kNT><<<(unsigned)std::min(std::max<int64_t>(chunks, 1), cap), kThreads, 0, st>>>(
-            x, n, ws, nslots);
+            x, n, word, 1);
     } else {
-        k_amax<DT, false, kAmaxK, false><<<(unsigned)std::min((n + 255) / 256, cap), kThreads, 0, st>>>(x, n, ws,
-                                                                                                       nslots);
+        k_amax<DT, false, kAmaxK, false><<<(unsigned)std::min((n + 255) / 256, cap), kThreads, 0, st>>>(x, n, word,
+                                                                                                       1);
     }
-    if (nslots > 1) k_fold_slots<<<1, 64, 0, st>>>(ws, nslots);
 }
 
 // The amax pass of a two-pass cast: at most kAmaxGrid workgroups, each
@@ -279,10 +279,10 @@ void launch_fill_f32(float* p, int64_t n, float v, hipStream_t st) {
     k_fill_f32<<<grid((n + kThreads - 1) / kThreads), kThreads, 0, st>>>(p, n, v);
 }
 
-void launch_amax(const void* x, int dt, int64_t n, uint32_t* ws, int nslots, hipStream_t st) {
-    if (dt == kF32) run_amax<kF32>(x, n, ws, nslots, st);
-    else if (dt == kBF16) run_amax<kBF16>(x, n, ws, nslots, st);
-    else run_amax<kF16>(x, n, ws, nslots, st);
+void launch_amax(const void* x, int dt, int64_t n, uint32_t* word, hipStream_t st) {
+    if (dt == kF32) run_amax<kF32>(x, n, word, st);
+    else if (dt == kBF16) run_amax<kBF16>(x, n, word, st);
+    else run_amax<kF16>(x, n, word, st);
 }
 
 int launch_amax_partials(const void* x, int dt, int64_t n, uint32_t* partial, hipStream_t st) {

@@ -14,17 +14,16 @@ enum { kE4M3 = 0, kE5M2 = 1 };
 // (checked by the ABI layer): sizes > 0 unless stated, pointers valid and
 // aligned to their element size, buffers non-overlapping.
 void launch_fill_f32(float* p, int64_t n, float v, hipStream_t st);
-// Amax slots (the stand-alone amax and the reduce step's re-cast): kAmaxSlots
-// words, kAmaxSlotStride words (128 bytes) apart; the finished amax is their
-// max, folded into slot 0.
+// Amax slots (the reduce step's re-cast): kAmaxSlots words, kAmaxSlotStride
+// words (128 bytes) apart; the finished amax is their max, folded into slot 0.
 constexpr int kAmaxSlots = 64;
 constexpr int kAmaxSlotStride = 32;
 // Amax partials (the two-pass casts): at most kAmaxPartials words, one per
 // workgroup of the amax pass; the cast pass folds them.
 constexpr int kAmaxPartials = 1024;
-// clears the nslots amax slots of ws, folds max |x| (binary32 bits) into them and
-// leaves the result in ws[0]; n may be 0
-void launch_amax(const void* x, int dt, int64_t n, uint32_t* ws, int nslots, hipStream_t st);
+// the stand-alone amax: clears *word, then folds max |x| (binary32 bits) into
+// it with one atomic max per workgroup; n may be 0
+void launch_amax(const void* x, int dt, int64_t n, uint32_t* word, hipStream_t st);
 // the amax pass of a two-pass cast: stores one partial max |x| per workgroup
 // to partial[0 .. np) and returns np (1 <= np <= kAmaxPartials); n may be 0
 int launch_amax_partials(const void* x, int dt, int64_t n, uint32_t* partial, hipStream_t st);

@@ -160,6 +160,35 @@ def test_packed_errors():
     assert d(None, E5, 3, 0, None, BF16, None) == fq.OK
 
 
+def test_reduce_step_errors():
+    d = L.fp8q_dequant_sum
+    #        q      fmt W  n   scale_inv       avg  y              ydt
+    assert d(P(A), E5, 0, 16, P(A + 8192), 0, P(A + 4096), BF16, None) == fq.EINVAL      # W < 1
+    assert d(P(A), E5, 2, -1, P(A + 8192), 0, P(A + 4096), BF16, None) == fq.EINVAL
+    assert d(P(A), E5, 2 ** 62, 0, P(A + 8192), 0, P(A + 4096), BF16, None) == fq.EINVAL  # W * 4 overflows
+    assert d(P(A), E5, 2 ** 40, 2 ** 40, P(A + 8192), 0, P(A + 4096), BF16, None) == fq.EINVAL
+    assert d(P(A), 2, 2, 16, P(A + 8192), 0, P(A + 4096), BF16, None) == fq.EDTYPE
+    assert d(P(A), E5, 2, 16, P(A + 8192), 0, P(A + 4096), 5, None) == fq.EDTYPE
+    assert d(P(A), E5, 2, 16, None, 0, P(A + 4096), BF16, None) == fq.EINVAL
+    assert d(P(A), E5, 2, 16, P(A + 8194), 0, P(A + 4096), BF16, None) == fq.EALIGN
+    assert d(P(A), E5, 2, 16, P(A + 8192), 0, P(A + 4097), BF16, None) == fq.EALIGN
+    assert d(P(A), E5, 2, 16, P(A + 8192), 0, P(A + 16), BF16, None) == fq.EINVAL        # y overlaps q
+    assert d(P(A), E5, 2, 16, P(A + 4100), 0, P(A + 4096), BF16, None) == fq.EINVAL      # scale_inv in y
+    assert d(None, E5, 3, 0, P(A + 8192), 0, None, BF16, None) == fq.OK
+    r = L.fp8q_dequant_sum_requant
+    ws = P(A + 65536)
+    #        q      fmt W  n   scale_inv       avg  y              ydt   q_out           sinv_out        ws
+    assert r(P(A), E5, 2, 16, P(A + 8192), 1, P(A + 4096), BF16, P(A + 12288), P(A + 16384), None, None) == fq.EINVAL
+    assert r(P(A), E5, 2, 16, P(A + 8192), 1, P(A + 4096), BF16, P(A + 12288), None, ws, None) == fq.EINVAL
+    assert r(P(A), E5, 2, 16, P(A + 8192), 1, P(A + 4096), BF16, None, P(A + 16384), ws, None) == fq.EINVAL
+    assert r(P(A), E5, 2, 16, P(A + 8192), 1, P(A + 4096), BF16, P(A + 12288), P(A + 16386), ws, None) == fq.EALIGN
+    assert r(P(A), E5, 2, 16, P(A + 8192), 1, P(A + 4096), BF16, P(A + 12288), P(A + 16384), P(A + 65537),
+             None) == fq.EALIGN
+    assert r(P(A), E5, 2, 16, P(A + 8192), 1, P(A + 4096), BF16, P(A + 12288), P(A + 16384), P(A + 4096),
+             None) == fq.EINVAL                                                                   # workspace = y
+    assert r(P(A), E5, 2, 16, P(A + 8192), 1, P(A + 4096), BF16, P(A + 4100), P(A + 16384), ws, None) == fq.EINVAL
+
+
 def test_python_binding_rejects_host_tensors():
     import torch
     x = torch.zeros((2, 128), dtype=torch.bfloat16)
