@@ -255,6 +255,7 @@ def main():
             "avg_launch_us": round(cast_avg, 3),
             "algorithmic_bytes_per_launch": cast_bytes,
         },
+        "roofline_block_dequant": _block_roofline(rows),
         "copy_reference": {"bytes": 2 * cp_n, "us": round(copy_us, 3), "gbps": round(copy_gbps, 1),
                            "same_volume_as_group_cast": {"bytes": 2 * cv_n, "us": round(cv_us, 3),
                                                           "gbps": round(2 * cv_n / (cv_us * 1e-6) / 1e9, 1)}},
@@ -279,10 +280,24 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(path=None):
-    """HBM bytes per launch of the group-cast kernel from the committed
-    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None when that summary is
-    missing or was taken on different kernel sources."""
+def _block_roofline(rows):
+    """The metric's second headline kernel, the 128x128 block dequant on the
+    weight workload, in the same form as `roofline` (events around each launch
+    after a read flush, from the rows)."""
+    r = rows.get("block128_dequant_e4m3fn_bf16_18432x7168")
+    if r is None:
+        return None
+    return {"kernel": "k_block128_flat (fp8q_weight_dequant_block128)", "bound": "hbm", "achieved": r["gbps"],
+            "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": r["frac_of_hbm_peak"],
+            "traffic": measured_traffic(kernel="k_block128_flat"), "avg_launch_us": r["avg_us"],
+            "algorithmic_bytes_per_launch": r["bytes"]}
+
+
+def measured_traffic(path=None, kernel=None):
+    """HBM bytes per launch of the group-cast kernel (or of `kernel`, e.g.
+    "k_block128_flat") from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summary, or None when that summary is missing or was taken on different
+    kernel sources."""
     import re
     if path is None:
         path = os.path.join(os.path.dirname(os.path.abspath(__file__)), TRAFFIC_SUMMARY)
@@ -291,7 +306,8 @@ def measured_traffic(path=None):
     except OSError:
         return None
     src = re.search(r"^kernel_sources_sha256:\s*([0-9a-f]{64})", text, re.M)
-    val = re.search(r"^hbm_bytes_per_launch:\s*([0-9.]+)", text, re.M)
+    key = "hbm_bytes_per_launch" if kernel is None else re.escape(f"hbm_bytes_per_launch[{kernel}]")
+    val = re.search(r"^" + key + r":\s*([0-9.]+)", text, re.M)
     if not src or not val or src.group(1) != kernel_source_hash():
         return None
     return float(val.group(1))

@@ -22,6 +22,12 @@ def test_traffic_summary_hash_gate(tmp_path):
     good = tmp_path / "good.md"
     good.write_text(f"# x\n\nhbm_bytes_per_launch: 356015025\nkernel_sources_sha256: {bench.kernel_source_hash()}\n")
     assert bench.measured_traffic(str(good)) == 356015025.0
+    both = tmp_path / "both.md"
+    both.write_text("hbm_bytes_per_launch: 356015025\nhbm_bytes_per_launch[k_block128_flat]: 396706335\n"
+                    f"kernel_sources_sha256: {bench.kernel_source_hash()}\n")
+    assert bench.measured_traffic(str(both), kernel="k_block128_flat") == 396706335.0
+    assert bench.measured_traffic(str(both)) == 356015025.0
+    assert bench.measured_traffic(str(good), kernel="k_block128_flat") is None
     stale = tmp_path / "stale.md"
     stale.write_text("hbm_bytes_per_launch: 356015025\nkernel_sources_sha256: " + "0" * 64 + "\n")
     assert bench.measured_traffic(str(stale)) is None
@@ -29,6 +35,8 @@ def test_traffic_summary_hash_gate(tmp_path):
     # the committed summary, whatever its state, parses to a number or None
     v = bench.measured_traffic()
     assert v is None or abs(v / 355991552 - 1) < 0.01
+    vb = bench.measured_traffic(kernel="k_block128_flat")
+    assert vb is None or abs(vb / (18432 * 7168 * 3 + 144 * 56 * 4) - 1) < 0.01
 
 
 def test_roundtrip_error_report():
