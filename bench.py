@@ -213,8 +213,10 @@ def main():
     torch.cuda.empty_cache()
 
     # ------------------------------------------------------------------ other rows
+    copy_ctx = {}
     if not args.no_rows:
-        rows.update(_other_rows(fq, W, np, torch, dev, st, args.rows_iters, log, HE, x0, roundtrip))
+        other, copy_ctx = _other_rows(fq, W, np, torch, dev, st, args.rows_iters, log, HE, x0, roundtrip)
+        rows.update(other)
     del x0
     HE.close()
 
@@ -258,7 +260,9 @@ def main():
         "roofline_block_dequant": _block_roofline(rows),
         "copy_reference": {"bytes": 2 * cp_n, "us": round(copy_us, 3), "gbps": round(copy_gbps, 1),
                            "same_volume_as_group_cast": {"bytes": 2 * cv_n, "us": round(cv_us, 3),
-                                                          "gbps": round(2 * cv_n / (cv_us * 1e-6) / 1e9, 1)}},
+                                                          "gbps": round(2 * cv_n / (cv_us * 1e-6) / 1e9, 1)},
+                           **{k: {"bytes": v["bytes"], "us": v["avg_us"], "gbps": v["gbps"]}
+                              for k, v in copy_ctx.items()}},
         "cpu_baseline": cpu,
         "roundtrip_rel_err": roundtrip,
         "rows": rows,
@@ -357,7 +361,7 @@ def _other_rows(fq, W, np, torch, dev, st, iters, log, HE, act, roundtrip):
     flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
     out = {}
 
-    def timed(name, nbytes, elems, fn):
+    def timed(name, nbytes, elems, fn, into=out):
         with torch.cuda.stream(st):
             fn()
             fn()
@@ -369,8 +373,8 @@ def _other_rows(fq, W, np, torch, dev, st, iters, log, HE, act, roundtrip):
                 fn()
                 HE.record(e1, st)
                 us.append(HE.us(e0, e1))
-        out[name] = _row(nbytes, us, elems)
-        log(f"{name}: {out[name]['avg_us']} us, {out[name]['gbps']} GB/s")
+        into[name] = _row(nbytes, us, elems)
+        log(f"{name}: {into[name]['avg_us']} us, {into[name]['gbps']} GB/s")
 
     # pipeline p2p cast of the activation (bf16 [16384, 7168]) with the format
     # chosen on the device, and back to bf16
@@ -484,9 +488,17 @@ def _other_rows(fq, W, np, torch, dev, st, iters, log, HE, act, roundtrip):
         timed(f"per_channel_dequant_e4m3fn_{dt}_4096x4096", R * C + R * 4 + R * C * esz, R * C,
               lambda: fq.fp8q_dequant_per_channel(q, sr, y, "e4m3fn", stream=st))
         del xd, q, y
+    # context for the short rows above: torch's device copy of the same byte
+    # volumes (half read, half written), timed the same way
+    ctx = {}
+    for label, nb in (("bf16_4096x4096_rows", 2 * R * C + R * C), ("f32_4096x4096_rows", 4 * R * C + R * C)):
+        a = torch.empty(nb // 2, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        timed(f"same_volume_as_{label}", 2 * (nb // 2), 2 * (nb // 2), lambda: b.copy_(a), into=ctx)
+        del a, b
     del flush
     torch.cuda.empty_cache()
-    return out
+    return out, ctx
 
 
 def _cpu_baseline(xh, R, C, G, log):
