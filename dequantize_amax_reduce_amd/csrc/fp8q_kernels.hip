@@ -9,9 +9,11 @@
 // one chunk of K = 2 sub-steps per workgroup with a grid covering the whole
 // tensor (measured faster than fewer, looping workgroups); non-temporal
 // loads and stores for the streaming data (1.5-1.8x faster than cached).
-// The amax pass is the exception: every workgroup ends in one atomic max on
-// a single word, and those serialise across the 8 XCDs, so its grid is
-// capped at kAmaxGrid workgroups that loop over chunks.
+// The amax passes are the exception: their grid is capped at kAmaxGrid
+// workgroups that loop over chunks.  In the stand-alone amax every workgroup
+// ends in one atomic max on a single word, and those serialise across the 8
+// XCDs; in the two-pass casts each workgroup stores one partial, and every
+// workgroup of the cast pass folds all of them.
 #include <algorithm>
 
 #include "fp8q_device.h"
