@@ -183,7 +183,8 @@ fp8q_status_t fp8q_cast_to_packed(const void* x, int xdtype, int64_t n, int fmt,
         return launched();
     }
     const int np = fp8q::launch_amax_partials(x, xdtype, n, (uint32_t*)workspace, S(stream));
-    fp8q::launch_tensor_cast(x, xdtype, n, fmt, (const uint32_t*)workspace, np, slot + 4, (float*)slot, S(stream));
+    fp8q::launch_tensor_cast(x, xdtype, n, fmt, (const uint32_t*)workspace, np, 1, slot + 4, (float*)slot,
+                             S(stream));
     return launched();
 }
 
@@ -219,7 +220,7 @@ fp8q_status_t fp8q_cast_per_tensor(const void* x, int xdtype, int64_t n, int fmt
         return launched();
     }
     const int np = fp8q::launch_amax_partials(x, xdtype, n, (uint32_t*)workspace, S(stream));
-    fp8q::launch_tensor_cast(x, xdtype, n, fmt, (const uint32_t*)workspace, np, q, scale_inv, S(stream));
+    fp8q::launch_tensor_cast(x, xdtype, n, fmt, (const uint32_t*)workspace, np, 1, q, scale_inv, S(stream));
     return launched();
 }
 
@@ -340,7 +341,9 @@ fp8q_status_t fp8q_dequant_sum_requant(const uint8_t* q, int fmt, int64_t W, int
         return launched();
     }
     fp8q::launch_dequant_sum(q, fmt, W, n, scale_inv, average, y, ydtype, (uint32_t*)workspace, S(stream));
-    fp8q::launch_tensor_cast(y, ydtype, n, fmt, (const uint32_t*)workspace, 1, q_out, scale_inv_out, S(stream), true);
+    // the cast pass folds the amax slots the sum pass left in the workspace
+    fp8q::launch_tensor_cast(y, ydtype, n, fmt, (const uint32_t*)workspace, fp8q::kAmaxSlots, fp8q::kAmaxSlotStride,
+                             q_out, scale_inv_out, S(stream), true);
     return launched();
 }
 

@@ -407,14 +407,6 @@ __global__ void k_guard_amax(uint32_t* p) {
     }
 }
 
-// fold the slots into slot 0 (one wavefront, after the stage-2 atomics), so
-// the cast pass reads a single word
-__global__ void k_fold_slots(uint32_t* p, int nslots) {
-    uint32_t m = (int)threadIdx.x < nslots ? p[threadIdx.x * kAmaxSlotStride] : 0u;
-    m = max_lanes<64>(m);
-    if (threadIdx.x == 0) p[0] = m;
-}
-
 __global__ void k_fill_f32(float* p, int64_t n, float v) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
         p[i] = v;
@@ -465,11 +457,14 @@ k_amax(const void* __restrict__ x, int64_t n, uint32_t* __restrict__ amax_bits, 
     }
 }
 
-// max over the np partials (binary32 bits of |x|); every thread of the
-// workgroup must call it (it contains barriers)
-__device__ __forceinline__ uint32_t fold_partials(const uint32_t* __restrict__ partial, int np, uint32_t* lds4) {
+// max over the np partials partial[0], partial[stride], ... (binary32 bits
+// of |x|: the amax pass's per-workgroup partials, stride 1, or the amax
+// slots, stride kAmaxSlotStride); every thread of the workgroup must call it
+// (it contains barriers)
+__device__ __forceinline__ uint32_t fold_partials(const uint32_t* __restrict__ partial, int np, int stride,
+                                                  uint32_t* lds4) {
     uint32_t a = 0;
-    for (int j = threadIdx.x; j < np; j += 256) a = umax(a, partial[j]);
+    for (int j = threadIdx.x; j < np; j += 256) a = umax(a, partial[j * stride]);
     return block_max256(a, lds4);
 }
 
@@ -566,15 +561,15 @@ __device__ __forceinline__ void cast_chunks(HpVec<DT>* v, const void* __restrict
 }
 
 // VEC: x 16-B aligned and q 4-byte aligned.  The amax is the max of the np
-// partials (np = 1: an already folded amax).
+// partials partial[0], partial[pstride], ...
 template <int DT, int FMT, bool VEC, int K, bool NT>
 __global__ void __launch_bounds__(256)
-k_tensor_cast(const void* __restrict__ x, int64_t n, const uint32_t* __restrict__ partial, int np,
+k_tensor_cast(const void* __restrict__ x, int64_t n, const uint32_t* __restrict__ partial, int np, int pstride,
               uint8_t* __restrict__ q, float* __restrict__ sinv_out) {
     __shared__ uint32_t lds[4];
     HpVec<DT> v[K];
     if constexpr (VEC) chunk_load<DT, K, NT>(v, x, n / LaneVE<DT>::value, blockIdx.x);
-    const uint32_t ab = fold_partials(partial, np, lds);
+    const uint32_t ab = fold_partials(partial, np, pstride, lds);
     float scale, sinv;
     tensor_scale<FMT>(ab, scale, sinv);
     if (blockIdx.x == 0 && threadIdx.x == 0) sinv_out[0] = sinv;
@@ -636,7 +631,7 @@ k_pipeline_cast(const void* __restrict__ x, int64_t n, const uint32_t* __restric
     __shared__ uint32_t lds[4];
     HpVec<DT> v[K];
     if constexpr (VEC) chunk_load<DT, K, NT>(v, x, n / LaneVE<DT>::value, blockIdx.x);
-    const uint32_t ab = fold_partials(partial, np, lds);
+    const uint32_t ab = fold_partials(partial, np, 1, lds);
     if (__uint_as_float(ab) > Fp8Fmt<kE4M3>::max)
         pipeline_cast_rest<DT, kE5M2, VEC, K, NT>(v, x, n, ab, q, sinv_out, fmt_out);
     else

@@ -77,15 +77,17 @@ template <int DT, int FMT> struct RunGroup128 {
 // cast pass whose input was just written by the previous kernel (the
 // reduce step's re-cast: 90.4 us against 93.1 us for 8 x 2^25 e5m2 chunks)
 template <int DT, int FMT> struct RunTensorCast {
-    static void run(const void* x, int64_t n, const uint32_t* partial, int np, uint8_t* q, float* sinv, bool cached,
-                    hipStream_t st) {
+    static void run(const void* x, int64_t n, const uint32_t* partial, int np, int pstride, uint8_t* q, float* sinv,
+                    bool cached, hipStream_t st) {
         constexpr int VE = LaneVE<DT>::value;
         const bool vec = al(x, 16) && al(q, 4);
         const unsigned nb = vec ? grid((n / VE + kFlatK * 256 - 1) / (kFlatK * 256)) : grid((n + 255) / 256);
         if (vec && cached)
-            k_tensor_cast<DT, FMT, true, kFlatK, false><<<nb, kThreads, 0, st>>>(x, n, partial, np, q, sinv);
-        else if (vec) k_tensor_cast<DT, FMT, true, kFlatK, kNT><<<nb, kThreads, 0, st>>>(x, n, partial, np, q, sinv);
-        else k_tensor_cast<DT, FMT, false, kFlatK, kNT><<<nb, kThreads, 0, st>>>(x, n, partial, np, q, sinv);
+            k_tensor_cast<DT, FMT, true, kFlatK, false><<<nb, kThreads, 0, st>>>(x, n, partial, np, pstride, q, sinv);
+        else if (vec)
+            k_tensor_cast<DT, FMT, true, kFlatK, kNT><<<nb, kThreads, 0, st>>>(x, n, partial, np, pstride, q, sinv);
+        else
+            k_tensor_cast<DT, FMT, false, kFlatK, kNT><<<nb, kThreads, 0, st>>>(x, n, partial, np, pstride, q, sinv);
     }
 };
 
@@ -262,7 +264,6 @@ template <int FMT, int YDT> struct RunDequantSum {
             // y is stored through the caches: the re-cast pass reads it next
             if (vec) k_dequant_sum<FMT, YDT, true, true, kNT, KV, false><<<nb, kThreads, 0, st>>>(q, W, n, sinv, average, y, ws, kAmaxSlots);
             else k_dequant_sum<FMT, YDT, false, true, kNT, KV><<<nb, kThreads, 0, st>>>(q, W, n, sinv, average, y, ws, kAmaxSlots);
-            k_fold_slots<<<1, 64, 0, st>>>(ws, kAmaxSlots);
         } else {
             if (vec) k_dequant_sum<FMT, YDT, true, false, kNT, KV><<<grid(units), kThreads, 0, st>>>(q, W, n, sinv, average, y, ws, 1);
             else k_dequant_sum<FMT, YDT, false, false, kNT, KV><<<grid(units), kThreads, 0, st>>>(q, W, n, sinv, average, y, ws, 1);
@@ -293,9 +294,9 @@ int launch_amax_partials(const void* x, int dt, int64_t n, uint32_t* partial, hi
     return run_amax_partials<kF16>(x, n, partial, st);
 }
 
-void launch_tensor_cast(const void* x, int dt, int64_t n, int fmt, const uint32_t* partial, int np, uint8_t* q,
-                        float* sinv, hipStream_t st, bool cached) {
-    dispatch_dt_fmt<RunTensorCast>(dt, fmt, x, n, partial, np, q, sinv, cached, st);
+void launch_tensor_cast(const void* x, int dt, int64_t n, int fmt, const uint32_t* partial, int np, int pstride,
+                        uint8_t* q, float* sinv, hipStream_t st, bool cached) {
+    dispatch_dt_fmt<RunTensorCast>(dt, fmt, x, n, partial, np, pstride, q, sinv, cached, st);
 }
 
 void launch_guard_amax(uint32_t* ws, hipStream_t st) { k_guard_amax<<<1, 64, 0, st>>>(ws); }

@@ -41,11 +41,12 @@ void launch_pipeline_cast(const void* x, int dt, int64_t n, const uint32_t* part
 // per-tensor dequant with the format read from fmt[0] on the device
 void launch_dequant_pipeline(const uint8_t* q, int64_t n, const float* sinv, const int32_t* fmt, void* y, int ydt,
                              hipStream_t st);
-// the scale-and-cast pass, with amax = max of partial[0 .. np) (np = 1: an
-// already folded amax).  cached: ordinary instead of non-temporal memory
-// accesses, for an input the previous kernel just wrote.
-void launch_tensor_cast(const void* x, int dt, int64_t n, int fmt, const uint32_t* partial, int np, uint8_t* q,
-                        float* sinv, hipStream_t st, bool cached = false);
+// the scale-and-cast pass, with amax = max of partial[0], partial[pstride],
+// ... (np words: the amax pass's partials with pstride 1, or the amax slots
+// with pstride kAmaxSlotStride).  cached: ordinary instead of non-temporal
+// memory accesses, for an input the previous kernel just wrote.
+void launch_tensor_cast(const void* x, int dt, int64_t n, int fmt, const uint32_t* partial, int np, int pstride,
+                        uint8_t* q, float* sinv, hipStream_t st, bool cached = false);
 void launch_channel_cast(const void* x, int dt, int64_t rows, int64_t cols, int fmt, uint8_t* q, float* sinv,
                          hipStream_t st);
 void launch_group128_cast(const void* x, int dt, int64_t groups, int fmt, uint8_t* q, float* sinv, hipStream_t st);
@@ -58,7 +59,8 @@ void launch_dequant_rows(const uint8_t* q, int fmt, int64_t rows, int64_t cols, 
 void launch_block128(const uint8_t* q, int fmt, int64_t M, int64_t N, const float* sinv, void* y, int ydt,
                      hipStream_t st);
 // y = chunk-ordered in-type sum of the W dequantized chunks of q (W x n), / W if average;
-// with ws != nullptr, the kAmaxSlots slots of ws are cleared first and max |y| ends in ws[0]
+// with ws != nullptr, the kAmaxSlots slots of ws are cleared first and max |y| ends in those slots
+// (their max: the cast pass folds them)
 void launch_dequant_sum(const uint8_t* q, int fmt, int64_t W, int64_t n, const float* sinv, int average, void* y,
                         int ydt, uint32_t* ws, hipStream_t st);
 
