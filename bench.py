@@ -171,6 +171,11 @@ def main():
         "group128_cast_bf16_e4m3fn_16384x7168": _row(cast_bytes, cast_us, R * C),
         "group128_dequant_e4m3fn_bf16_16384x7168": _row(deq_bytes, deq_us, R * C),
     }
+    # context for the roofline: the cast alone, back to back over the rotating
+    # sets with one event pair per batch, i.e. its launch duration without a
+    # pair of event records around every launch
+    cast_b2b = _back_to_back(HE, st, NSETS, lambda i: fq.fp8q_cast_per_group128(
+        sets[i % NSETS]["x"], sets[i % NSETS]["q"], sets[i % NSETS]["s"], "e4m3fn", stream=st))
     # round-trip error of the step's own output (outside the timed region)
     b0 = sets[(args.steps - 1) % NSETS]                 # written by the last timed step
     roundtrip = {"group128_e4m3fn_bf16_16384x7168": _roundtrip_err(
@@ -256,6 +261,7 @@ def main():
             "traffic": measured_traffic(),
             "avg_launch_us": round(cast_avg, 3),
             "algorithmic_bytes_per_launch": cast_bytes,
+            "back_to_back": _b2b_summary(cast_bytes, cast_b2b),
         },
         "roofline_block_dequant": _block_roofline(rows),
         "copy_reference": {"bytes": 2 * cp_n, "us": round(copy_us, 3), "gbps": round(copy_gbps, 1),
@@ -294,7 +300,7 @@ def _block_roofline(rows):
     return {"kernel": "k_block128_flat (fp8q_weight_dequant_block128)", "bound": "hbm", "achieved": r["gbps"],
             "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": r["frac_of_hbm_peak"],
             "traffic": measured_traffic(kernel="k_block128_flat"), "avg_launch_us": r["avg_us"],
-            "algorithmic_bytes_per_launch": r["bytes"]}
+            "algorithmic_bytes_per_launch": r["bytes"], "back_to_back": r.get("back_to_back")}
 
 
 def measured_traffic(path=None, kernel=None):
@@ -315,6 +321,34 @@ def measured_traffic(path=None, kernel=None):
     if not src or not val or src.group(1) != kernel_source_hash():
         return None
     return float(val.group(1))
+
+
+def _back_to_back(HE, st, nsets, fn, batches=5, per=12):
+    """Per-launch time of fn(i) launched `per` times back to back (i cycling
+    over the rotating buffer sets) between one pair of events; one value per
+    batch, after one untimed round."""
+    import torch
+    us = []
+    with torch.cuda.stream(st):
+        for i in range(nsets):
+            fn(i)
+        for _ in range(batches):
+            e0, e1 = HE.new(), HE.new()
+            HE.record(e0, st)
+            for i in range(per):
+                fn(i)
+            HE.record(e1, st)
+            us.append(HE.us(e0, e1) / per)
+    return us
+
+
+def _b2b_summary(nbytes, us_list):
+    import numpy as np
+    med = float(np.median(us_list))
+    return {"median_launch_us": round(med, 3), "min_launch_us": round(float(np.min(us_list)), 3),
+            "frac": round(nbytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "protocol": f"{len(us_list)} batches of back-to-back launches over rotating buffer sets, "
+                        "one event pair per batch"}
 
 
 def _row(nbytes, us_list, elems):
@@ -397,9 +431,13 @@ def _other_rows(fq, W, np, torch, dev, st, iters, log, HE, act, roundtrip):
     qd = torch.from_numpy(ch).to(dev)
     sd = torch.from_numpy(sh).to(dev)
     yd = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    timed("block128_dequant_e4m3fn_bf16_18432x7168", M * N + sd.numel() * 4 + M * N * 2, M * N,
+    blk_bytes = M * N + sd.numel() * 4 + M * N * 2
+    timed("block128_dequant_e4m3fn_bf16_18432x7168", blk_bytes, M * N,
           lambda: fq.fp8q_weight_dequant_block128(qd, sd, yd, "e4m3fn", stream=st))
-    del qd, sd, yd, ch
+    qs, ys = [qd, qd.clone(), qd.clone()], [yd, torch.empty_like(yd), torch.empty_like(yd)]
+    out["block128_dequant_e4m3fn_bf16_18432x7168"]["back_to_back"] = _b2b_summary(blk_bytes, _back_to_back(
+        HE, st, 3, lambda i: fq.fp8q_weight_dequant_block128(qs[i % 3], sd, ys[i % 3], "e4m3fn", stream=st)))
+    del qd, sd, yd, ch, qs, ys
 
     # per-tensor e5m2 on the 1-D gradient payload bf16 [2^28]
     log("gradient payload workload")
