@@ -359,12 +359,21 @@ def fp8q_dequant_sum_requant(q, scale_inv, y, q_out, scale_inv_out, workspace, f
 # page-level helpers (allocate outputs with torch; all compute in the kernels)
 # ---------------------------------------------------------------------------
 
-def cast_to_fp8(inp: torch.Tensor, fp8_format="e4m3", per_channel_scale=False):
+def cast_to_fp8(inp: torch.Tensor, fp8_format="e4m3", per_channel_scale=False, out=None):
     """(fp8 tensor, scale_inv) -- ColossalAI fp8.py cast_to_fp8.  scale_inv is
-    float32[1] per-tensor or float32[rows] per-channel (row-indexed)."""
+    float32[1] per-tensor or float32[rows] per-channel (row-indexed).  With
+    `out` (an fp8 tensor of fp8_format, or uint8 codes, with inp's number of
+    elements) the codes are written there and `out` is returned, as the page's
+    torch.mul(scale, inp.float(), out=out) does."""
     f = _fmt(fp8_format)
     _hp_dtype(inp, "inp")
-    q = torch.empty(inp.shape, dtype=_FP8_DTYPE[f], device=inp.device)
+    if out is not None:
+        _fp8(out, f, "out")
+        if out.numel() != inp.numel():
+            raise ValueError("cast_to_fp8: out must have as many elements as inp")
+        q = out
+    else:
+        q = torch.empty(inp.shape, dtype=_FP8_DTYPE[f], device=inp.device)
     if per_channel_scale:
         rows, _ = _rows_cols(inp)
         sinv = torch.empty(rows, dtype=torch.float32, device=inp.device)
@@ -376,11 +385,19 @@ def cast_to_fp8(inp: torch.Tensor, fp8_format="e4m3", per_channel_scale=False):
     return q, sinv
 
 
-def cast_from_fp8(inp: torch.Tensor, scale_inv: torch.Tensor, ret_type: torch.dtype, per_channel_scale=False):
-    """ColossalAI fp8.py cast_from_fp8: ret_type(fp32(inp) * scale_inv)."""
+def cast_from_fp8(inp: torch.Tensor, scale_inv: torch.Tensor, ret_type: torch.dtype, per_channel_scale=False,
+                  out=None):
+    """ColossalAI fp8.py cast_from_fp8: ret_type(fp32(inp) * scale_inv).  With
+    `out`, the result is written there in out's own dtype and `out` is
+    returned (the page's torch.mul(scale_inv, inp.float(), out=out))."""
     if inp.dtype not in (torch.float8_e4m3fn, torch.float8_e5m2):
         raise TypeError("Only float8_e4m3fn and float8_e5m2 are allowed.")
-    y = torch.empty(inp.shape, dtype=ret_type, device=inp.device)
+    if out is not None:
+        if out.numel() != inp.numel():
+            raise ValueError("cast_from_fp8: out must have as many elements as inp")
+        y = out
+    else:
+        y = torch.empty(inp.shape, dtype=ret_type, device=inp.device)
     if per_channel_scale:
         fp8q_dequant_per_channel(inp, scale_inv.reshape(-1), y)
     else:

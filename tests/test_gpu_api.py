@@ -26,6 +26,21 @@ def test_cast_to_from_fp8_helpers():
             y = fq.cast_from_fp8(q, s, torch.bfloat16, per_channel_scale=per_channel)
             deq = oracle.dequant_per_channel if per_channel else oracle.dequant_per_tensor
             assert_hp_equal(host(y), deq(wq, tfmt, ws, "bf16"), "bf16")
+            # the out= forms write into the caller's tensors and return them;
+            # cast_from_fp8 takes out's dtype (fp32 here), as torch.mul(..., out=out) does
+            qo = torch.full(x.shape, 0x55, dtype=torch.uint8, device="cuda:0")
+            r, s2 = fq.cast_to_fp8(x, fmt, per_channel_scale=per_channel, out=qo)
+            assert r is qo
+            assert_fp8_equal(host(qo), wq, tfmt)
+            assert_f32_equal(host(s2), ws)
+            yo = torch.full(x.shape, 7.0, dtype=torch.float32, device="cuda:0")
+            r = fq.cast_from_fp8(q, s, torch.bfloat16, per_channel_scale=per_channel, out=yo)
+            assert r is yo
+            assert_f32_equal(host(yo), deq(wq, tfmt, ws, "f32"))
+    with pytest.raises(TypeError):   # out of the other fp8 format
+        fq.cast_to_fp8(dev(xb, "bf16"), "e4m3", out=torch.empty(xb.shape, dtype=torch.float8_e5m2, device="cuda:0"))
+    with pytest.raises(ValueError):  # out of the wrong size
+        fq.cast_from_fp8(q, s, torch.bfloat16, out=torch.empty(5, dtype=torch.float32, device="cuda:0"))
 
 
 def test_per_token_and_weight_dequant_helpers():
