@@ -93,6 +93,9 @@ def parse():
 
 def main():
     args = parse()
+    if args.steps < 1 or args.warmup < 0 or args.rows_iters < 1:
+        print("bench.py: --steps and --rows-iters must be >= 1 and --warmup >= 0", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1:
         print(f"bench.py: fp8q measures one GPU only; --gpus {args.gpus} is not supported (the row, group and "
               "block kernels would shard by rows with no exchange, so a multi-GPU run is N independent copies)",

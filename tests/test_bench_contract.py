@@ -18,6 +18,12 @@ def test_more_than_one_gpu_is_refused():
     assert "one GPU" in r.stderr and r.stdout == ""
 
 
+def test_bench_rejects_empty_timed_region():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "0"], capture_output=True,
+                       text=True, cwd=ROOT)
+    assert r.returncode == 2 and r.stdout == ""
+
+
 def test_traffic_summary_hash_gate(tmp_path):
     good = tmp_path / "good.md"
     good.write_text(f"# x\n\nhbm_bytes_per_launch: 356015025\nkernel_sources_sha256: {bench.kernel_source_hash()}\n")
