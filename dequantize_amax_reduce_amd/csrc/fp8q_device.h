@@ -965,12 +965,15 @@ __device__ __forceinline__ uint32_t div_u32(uint32_t n, DivU32 d) {
 // its row by an invariant-divisor division of its lane-vector index by the
 // lane vectors per row (vpr), and reads its tile's scale_inv from the cached
 // scale row.  Requires N % VE == 0, q 4-byte aligned, y 16-B aligned and
-// M * N / VE < 2^32.
+// M * N / VE < 2^32.  The block column is the lane-vector column divided by
+// the lane vectors per 128 columns (LVB), never col * VE / 128: a single row
+// may hold 2^32 or more elements, where col * VE leaves 32 bits.
 template <int FMT, int YDT, int K, bool NT>
 __global__ void __launch_bounds__(256)
 k_block128_flat(const uint8_t* __restrict__ q, int64_t nvec, const float* __restrict__ sinv,
                 void* __restrict__ y, int64_t nbn, uint32_t vpr, DivU32 dvpr) {
     constexpr int VE = LaneVE<YDT>::value;
+    constexpr uint32_t LVB = 128 / VE;   // lane vectors per 128-column block (a power of two)
     const int64_t nchunks = (nvec + K * 256 - 1) / (K * 256);
     for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
         Fp8Vec<FMT, VE, NT> w[K];
@@ -985,7 +988,7 @@ k_block128_flat(const uint8_t* __restrict__ q, int64_t nvec, const float* __rest
             if (vi < nvec) {
                 const uint32_t row = div_u32((uint32_t)vi, dvpr);
                 const uint32_t col = (uint32_t)vi - row * vpr;          // lane vector within the row
-                const float s = sinv[(int64_t)(row >> 7) * nbn + ((col * VE) >> 7)];
+                const float s = sinv[(int64_t)(row >> 7) * nbn + col / LVB];
                 float p[VE];
                 w[k].decode_scaled(s, p);
                 store_out16<YDT, NT>(y, vi * VE, p);

@@ -126,3 +126,37 @@ def test_block_dequant_row_strip_path():
     want = oracle.dequant_per_channel(cs.reshape(-1, 1), "e4m3fn", sh[ii // 128, jj // 128], "bf16").reshape(-1)
     assert_hp_equal(ys, want, "bf16", "sampled block dequant")
     _free(c, s, y)
+
+
+@pytest.mark.parametrize("ydt", ["bf16", "f32"])
+def test_block_dequant_single_row_beyond_2_32_columns(ydt):
+    """One row of 2^32 + 1024 codes: few enough lane vectors for the flat
+    kernel, but the column of an element past 2^32 no longer fits 32 bits,
+    so its 128-column block must be found without forming col * VE.  The
+    scale index is pid_m * ceil(N/128) + pid_n (CSDN notes, weight_dequant_kernel)."""
+    M, N = 1, (1 << 32) + 1024
+    esz = 2 if ydt == "bf16" else 4
+    _need(4 + 4 * esz + 2)
+    print(f"[case] block dequant [{M}, {N}] -> {ydt}", flush=True)
+    c = torch.randint(0, 254, (M, N), generator=_gen(87), device=DEV, dtype=torch.uint8)
+    flat = c.view(-1)
+    for i0 in range(0, N, 1 << 30):        # no NaN code (0x7F, 0xFF); bounded temporaries
+        blk = flat[i0:i0 + (1 << 30)]
+        blk += (blk >= 0x7F).to(torch.uint8)
+    torch.cuda.empty_cache()
+    nb = (N + 127) // 128
+    rng = np.random.Generator(np.random.PCG64(88))
+    sh = (10.0 ** rng.uniform(-4.0, -1.0, size=(1, nb))).astype(np.float32)
+    s = torch.from_numpy(sh).to(DEV)
+    y = torch.empty((M, N), dtype=torch.bfloat16 if ydt == "bf16" else torch.float32, device=DEV)
+    fq.fp8q_weight_dequant_block128(c, s, y, "e4m3fn")
+    torch.cuda.synchronize()
+    jj = np.unique(np.concatenate([np.arange(0, 300), np.arange((1 << 32) - 300, (1 << 32) + 300),
+                                   np.arange(N - 300, N), rng.integers(0, N, 4000),
+                                   rng.integers(1 << 32, N, 500)]))
+    ti = torch.from_numpy(jj).to(DEV)
+    cs = _bits(flat[ti])
+    ys = _bits(y.view(-1)[ti])
+    want = oracle.dequant_per_channel(cs.reshape(-1, 1), "e4m3fn", sh[0, jj // 128], ydt).reshape(-1)
+    assert_hp_equal(ys, want, ydt, "sampled single-row block dequant")
+    _free(c, s, y)
