@@ -53,7 +53,7 @@ fp8q_status_t launched() { return hipGetLastError() == hipSuccess ? FP8Q_OK : FP
 hipStream_t S(void* s) { return (hipStream_t)s; }
 
 // common checks of a 2-D [rows, cols] high-precision <-> fp8 pair
-fp8q_status_t check_2d(const void* hp, int hpdt, int64_t rows, int64_t cols, int fmt, const void* q,
+fp8q_status_t check_2d(const void* hp, int hpdt, int64_t rows, int64_t cols, fp8q_fmt_t fmt, const void* q,
                        const float* sinv, int64_t sinv_count, int64_t* n_out) {
     if (!valid_dtype(hpdt) || !valid_fmt(fmt)) return FP8Q_EDTYPE;
     int64_t n, hpbytes, sbytes;
@@ -74,7 +74,7 @@ extern "C" {
 
 int fp8q_abi_version(void) { return FP8Q_ABI_VERSION; }
 
-const char* fp8q_status_str(int status) {
+const char* fp8q_status_str(fp8q_status_t status) {
     switch (status) {
         case FP8Q_OK: return "FP8Q_OK";
         case FP8Q_EINVAL: return "FP8Q_EINVAL: invalid size, NULL pointer or overlapping buffers";
@@ -91,7 +91,7 @@ size_t fp8q_per_tensor_workspace_bytes(void) {
     return sizeof(uint32_t) * fp8q::kAmaxSlots * fp8q::kAmaxSlotStride;
 }
 
-fp8q_status_t fp8q_amax(const void* x, int xdtype, int64_t n, float* amax, void* stream) {
+fp8q_status_t fp8q_amax(const void* x, fp8q_dtype_t xdtype, int64_t n, float* amax, void* stream) {
     if (!valid_dtype(xdtype)) return FP8Q_EDTYPE;
     int64_t xbytes;
     if (n < 0 || !mul_ok(n, esize(xdtype), &xbytes)) return FP8Q_EINVAL;
@@ -102,14 +102,14 @@ fp8q_status_t fp8q_amax(const void* x, int xdtype, int64_t n, float* amax, void*
     return launched();
 }
 
-fp8q_status_t fp8q_amax_guarded(const void* x, int xdtype, int64_t n, float* amax, void* stream) {
+fp8q_status_t fp8q_amax_guarded(const void* x, fp8q_dtype_t xdtype, int64_t n, float* amax, void* stream) {
     fp8q_status_t st = fp8q_amax(x, xdtype, n, amax, stream);
     if (st != FP8Q_OK) return st;
     fp8q::launch_guard_amax((uint32_t*)amax, S(stream));
     return launched();
 }
 
-fp8q_status_t fp8q_cast_with_amax(const void* x, int xdtype, int64_t n, int fmt, const float* amax, uint8_t* q,
+fp8q_status_t fp8q_cast_with_amax(const void* x, fp8q_dtype_t xdtype, int64_t n, fp8q_fmt_t fmt, const float* amax, uint8_t* q,
                                   float* scale_out, void* stream) {
     if (n < 0) return FP8Q_EINVAL;
     int64_t nn;
@@ -124,7 +124,7 @@ fp8q_status_t fp8q_cast_with_amax(const void* x, int xdtype, int64_t n, int fmt,
     return launched();
 }
 
-fp8q_status_t fp8q_dequant_div_scale(const uint8_t* q, int fmt, int64_t n, const float* scale, void* y, int ydtype,
+fp8q_status_t fp8q_dequant_div_scale(const uint8_t* q, fp8q_fmt_t fmt, int64_t n, const float* scale, void* y, fp8q_dtype_t ydtype,
                                      void* stream) {
     if (n < 0) return FP8Q_EINVAL;
     int64_t nn;
@@ -135,7 +135,7 @@ fp8q_status_t fp8q_dequant_div_scale(const uint8_t* q, int fmt, int64_t n, const
     return launched();
 }
 
-fp8q_status_t fp8q_cast_to_fp8_pipeline(const void* x, int xdtype, int64_t n, uint8_t* q, float* scale_inv,
+fp8q_status_t fp8q_cast_to_fp8_pipeline(const void* x, fp8q_dtype_t xdtype, int64_t n, uint8_t* q, float* scale_inv,
                                         int32_t* fmt_out, void* workspace, void* stream) {
     if (n < 0) return FP8Q_EINVAL;
     int64_t nn;
@@ -154,7 +154,7 @@ fp8q_status_t fp8q_cast_to_fp8_pipeline(const void* x, int xdtype, int64_t n, ui
 }
 
 fp8q_status_t fp8q_cast_from_fp8_pipeline(const uint8_t* q, const int32_t* fmt, int64_t n, const float* scale_inv,
-                                          void* y, int ydtype, void* stream) {
+                                          void* y, fp8q_dtype_t ydtype, void* stream) {
     if (n < 0) return FP8Q_EINVAL;
     int64_t nn;
     fp8q_status_t st = check_2d(y, ydtype, 1, n, FP8Q_E4M3FN, q, scale_inv, n > 0 ? 1 : 0, &nn);
@@ -168,7 +168,7 @@ fp8q_status_t fp8q_cast_from_fp8_pipeline(const uint8_t* q, const int32_t* fmt, 
     return launched();
 }
 
-fp8q_status_t fp8q_cast_to_packed(const void* x, int xdtype, int64_t n, int fmt, uint8_t* slot, void* workspace,
+fp8q_status_t fp8q_cast_to_packed(const void* x, fp8q_dtype_t xdtype, int64_t n, fp8q_fmt_t fmt, uint8_t* slot, void* workspace,
                                   void* stream) {
     if (!valid_dtype(xdtype) || !valid_fmt(fmt)) return FP8Q_EDTYPE;
     int64_t xbytes;
@@ -188,7 +188,7 @@ fp8q_status_t fp8q_cast_to_packed(const void* x, int xdtype, int64_t n, int fmt,
     return launched();
 }
 
-fp8q_status_t fp8q_dequant_packed(const uint8_t* slots, int fmt, int64_t W, int64_t n, void* y, int ydtype,
+fp8q_status_t fp8q_dequant_packed(const uint8_t* slots, fp8q_fmt_t fmt, int64_t W, int64_t n, void* y, fp8q_dtype_t ydtype,
                                   void* stream) {
     if (!valid_dtype(ydtype) || !valid_fmt(fmt)) return FP8Q_EDTYPE;
     int64_t sbytes, ybytes;
@@ -204,7 +204,7 @@ fp8q_status_t fp8q_dequant_packed(const uint8_t* slots, int fmt, int64_t W, int6
     return launched();
 }
 
-fp8q_status_t fp8q_cast_per_tensor(const void* x, int xdtype, int64_t n, int fmt, uint8_t* q, float* scale_inv,
+fp8q_status_t fp8q_cast_per_tensor(const void* x, fp8q_dtype_t xdtype, int64_t n, fp8q_fmt_t fmt, uint8_t* q, float* scale_inv,
                                    void* workspace, void* stream) {
     if (n < 0) return FP8Q_EINVAL;
     int64_t nn;
@@ -224,7 +224,7 @@ fp8q_status_t fp8q_cast_per_tensor(const void* x, int xdtype, int64_t n, int fmt
     return launched();
 }
 
-fp8q_status_t fp8q_cast_per_channel(const void* x, int xdtype, int64_t rows, int64_t cols, int fmt, uint8_t* q,
+fp8q_status_t fp8q_cast_per_channel(const void* x, fp8q_dtype_t xdtype, int64_t rows, int64_t cols, fp8q_fmt_t fmt, uint8_t* q,
                                     float* scale_inv, void* stream) {
     int64_t n;
     fp8q_status_t st = check_2d(x, xdtype, rows, cols, fmt, q, scale_inv, rows, &n);
@@ -238,7 +238,7 @@ fp8q_status_t fp8q_cast_per_channel(const void* x, int xdtype, int64_t rows, int
     return launched();
 }
 
-fp8q_status_t fp8q_cast_per_group128(const void* x, int xdtype, int64_t rows, int64_t cols, int fmt, uint8_t* q,
+fp8q_status_t fp8q_cast_per_group128(const void* x, fp8q_dtype_t xdtype, int64_t rows, int64_t cols, fp8q_fmt_t fmt, uint8_t* q,
                                      float* scale_inv, void* stream) {
     if (!valid_dtype(xdtype) || !valid_fmt(fmt)) return FP8Q_EDTYPE;
     if (rows < 0 || cols < 0) return FP8Q_EINVAL;
@@ -253,8 +253,8 @@ fp8q_status_t fp8q_cast_per_group128(const void* x, int xdtype, int64_t rows, in
     return launched();
 }
 
-fp8q_status_t fp8q_dequant_per_tensor(const uint8_t* q, int fmt, int64_t n, const float* scale_inv, void* y,
-                                      int ydtype, void* stream) {
+fp8q_status_t fp8q_dequant_per_tensor(const uint8_t* q, fp8q_fmt_t fmt, int64_t n, const float* scale_inv, void* y,
+                                      fp8q_dtype_t ydtype, void* stream) {
     if (n < 0) return FP8Q_EINVAL;
     int64_t nn;
     fp8q_status_t st = check_2d(y, ydtype, 1, n, fmt, q, scale_inv, n > 0 ? 1 : 0, &nn);
@@ -264,8 +264,8 @@ fp8q_status_t fp8q_dequant_per_tensor(const uint8_t* q, int fmt, int64_t n, cons
     return launched();
 }
 
-fp8q_status_t fp8q_dequant_per_channel(const uint8_t* q, int fmt, int64_t rows, int64_t cols,
-                                       const float* scale_inv, void* y, int ydtype, void* stream) {
+fp8q_status_t fp8q_dequant_per_channel(const uint8_t* q, fp8q_fmt_t fmt, int64_t rows, int64_t cols,
+                                       const float* scale_inv, void* y, fp8q_dtype_t ydtype, void* stream) {
     int64_t n;
     fp8q_status_t st = check_2d(y, ydtype, rows, cols, fmt, q, scale_inv, cols > 0 ? rows : 0, &n);
     if (st != FP8Q_OK) return st;
@@ -274,8 +274,8 @@ fp8q_status_t fp8q_dequant_per_channel(const uint8_t* q, int fmt, int64_t rows, 
     return launched();
 }
 
-fp8q_status_t fp8q_dequant_per_group128(const uint8_t* q, int fmt, int64_t rows, int64_t cols,
-                                        const float* scale_inv, void* y, int ydtype, void* stream) {
+fp8q_status_t fp8q_dequant_per_group128(const uint8_t* q, fp8q_fmt_t fmt, int64_t rows, int64_t cols,
+                                        const float* scale_inv, void* y, fp8q_dtype_t ydtype, void* stream) {
     if (!valid_dtype(ydtype) || !valid_fmt(fmt)) return FP8Q_EDTYPE;
     if (rows < 0 || cols < 0) return FP8Q_EINVAL;
     if (cols % 128 != 0) return FP8Q_ESHAPE;
@@ -289,8 +289,8 @@ fp8q_status_t fp8q_dequant_per_group128(const uint8_t* q, int fmt, int64_t rows,
     return launched();
 }
 
-fp8q_status_t fp8q_weight_dequant_block128(const uint8_t* q, int fmt, int64_t M, int64_t N,
-                                           const float* scale_inv, void* y, int ydtype, void* stream) {
+fp8q_status_t fp8q_weight_dequant_block128(const uint8_t* q, fp8q_fmt_t fmt, int64_t M, int64_t N,
+                                           const float* scale_inv, void* y, fp8q_dtype_t ydtype, void* stream) {
     if (M < 0 || N < 0) return FP8Q_EINVAL;
     int64_t nscale;  // ceil(M/128) * ceil(N/128), without overflowing M + 127
     if (!mul_ok(M / 128 + (M % 128 != 0), N / 128 + (N % 128 != 0), &nscale)) return FP8Q_EINVAL;
@@ -303,8 +303,8 @@ fp8q_status_t fp8q_weight_dequant_block128(const uint8_t* q, int fmt, int64_t M,
 }
 
 // shared validation of the reduce-step entry points
-static fp8q_status_t check_sum(const uint8_t* q, int fmt, int64_t W, int64_t n, const float* scale_inv, const void* y,
-                               int ydtype, int64_t* qbytes, int64_t* ybytes, int64_t* sbytes) {
+static fp8q_status_t check_sum(const uint8_t* q, fp8q_fmt_t fmt, int64_t W, int64_t n, const float* scale_inv, const void* y,
+                               fp8q_dtype_t ydtype, int64_t* qbytes, int64_t* ybytes, int64_t* sbytes) {
     if (!valid_dtype(ydtype) || !valid_fmt(fmt)) return FP8Q_EDTYPE;
     if (W < 1 || n < 0 || !mul_ok(W, n, qbytes) || !mul_ok(n, esize(ydtype), ybytes) || !mul_ok(W, 4, sbytes))
         return FP8Q_EINVAL;
@@ -313,8 +313,8 @@ static fp8q_status_t check_sum(const uint8_t* q, int fmt, int64_t W, int64_t n, 
     return FP8Q_OK;
 }
 
-fp8q_status_t fp8q_dequant_sum(const uint8_t* q, int fmt, int64_t W, int64_t n, const float* scale_inv, int average,
-                               void* y, int ydtype, void* stream) {
+fp8q_status_t fp8q_dequant_sum(const uint8_t* q, fp8q_fmt_t fmt, int64_t W, int64_t n, const float* scale_inv, int average,
+                               void* y, fp8q_dtype_t ydtype, void* stream) {
     int64_t qbytes, ybytes, sbytes;
     fp8q_status_t st = check_sum(q, fmt, W, n, scale_inv, y, ydtype, &qbytes, &ybytes, &sbytes);
     if (st != FP8Q_OK) return st;
@@ -325,8 +325,8 @@ fp8q_status_t fp8q_dequant_sum(const uint8_t* q, int fmt, int64_t W, int64_t n, 
     return launched();
 }
 
-fp8q_status_t fp8q_dequant_sum_requant(const uint8_t* q, int fmt, int64_t W, int64_t n, const float* scale_inv,
-                                       int average, void* y, int ydtype, uint8_t* q_out, float* scale_inv_out,
+fp8q_status_t fp8q_dequant_sum_requant(const uint8_t* q, fp8q_fmt_t fmt, int64_t W, int64_t n, const float* scale_inv,
+                                       int average, void* y, fp8q_dtype_t ydtype, uint8_t* q_out, float* scale_inv_out,
                                        void* workspace, void* stream) {
     int64_t qbytes, ybytes, sbytes;
     fp8q_status_t st = check_sum(q, fmt, W, n, scale_inv, y, ydtype, &qbytes, &ybytes, &sbytes);

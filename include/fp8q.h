@@ -66,7 +66,7 @@ typedef enum {
 int fp8q_abi_version(void);
 
 /* static, human-readable name of a status code (never NULL) */
-const char* fp8q_status_str(int status);
+const char* fp8q_status_str(fp8q_status_t status);
 
 /* bytes of device workspace (8192) that fp8q_cast_per_tensor,
  * fp8q_cast_to_fp8_pipeline, fp8q_cast_to_packed and fp8q_dequant_sum_requant
@@ -82,7 +82,7 @@ size_t fp8q_per_tensor_workspace_bytes(void);
  * n == 0 gives +0.  Two stages: a per-workgroup reduction, then an atomic max
  * on the binary32 bits into amax[0], which the call first clears on `stream`.
  */
-fp8q_status_t fp8q_amax(const void* x, int xdtype, int64_t n, float* amax, void* stream);
+fp8q_status_t fp8q_amax(const void* x, fp8q_dtype_t xdtype, int64_t n, float* amax, void* stream);
 
 /*
  * Per-tensor cast (ColossalAI fp8.py, cast_to_fp8 with per_channel_scale=False).
@@ -94,7 +94,7 @@ fp8q_status_t fp8q_amax(const void* x, int xdtype, int64_t n, float* amax, void*
  * else (cast_to_fp8's empty-tensor branch).  Reads x twice (amax pass, then
  * the scale-and-cast pass).
  */
-fp8q_status_t fp8q_cast_per_tensor(const void* x, int xdtype, int64_t n, int fmt,
+fp8q_status_t fp8q_cast_per_tensor(const void* x, fp8q_dtype_t xdtype, int64_t n, fp8q_fmt_t fmt,
                                    uint8_t* q, float* scale_inv, void* workspace, void* stream);
 
 /*
@@ -106,7 +106,7 @@ fp8q_status_t fp8q_cast_per_tensor(const void* x, int xdtype, int64_t n, int fmt
  * scale_inv has `rows` floats (row-indexed).  rows == 0 is a no-op; cols == 0
  * writes scale_inv[r] = 1.0 for every row (the empty-tensor branch).
  */
-fp8q_status_t fp8q_cast_per_channel(const void* x, int xdtype, int64_t rows, int64_t cols, int fmt,
+fp8q_status_t fp8q_cast_per_channel(const void* x, fp8q_dtype_t xdtype, int64_t rows, int64_t cols, fp8q_fmt_t fmt,
                                     uint8_t* q, float* scale_inv, void* stream);
 
 /*
@@ -119,7 +119,7 @@ fp8q_status_t fp8q_cast_per_channel(const void* x, int xdtype, int64_t rows, int
  * cols % 128 != 0 -> FP8Q_ESHAPE.  scale_inv is [rows, cols/128] row-major.
  * rows == 0 or cols == 0 is a no-op.
  */
-fp8q_status_t fp8q_cast_per_group128(const void* x, int xdtype, int64_t rows, int64_t cols, int fmt,
+fp8q_status_t fp8q_cast_per_group128(const void* x, fp8q_dtype_t xdtype, int64_t rows, int64_t cols, fp8q_fmt_t fmt,
                                      uint8_t* q, float* scale_inv, void* stream);
 
 /*
@@ -127,15 +127,15 @@ fp8q_status_t fp8q_cast_per_group128(const void* x, int xdtype, int64_t rows, in
  *   y[i] = ydtype(fp32(q[i]) * scale_inv[0]) -- the binary32 product rounded
  * once more to bf16/fp16 when ydtype is not F32.  n == 0 is a no-op.
  */
-fp8q_status_t fp8q_dequant_per_tensor(const uint8_t* q, int fmt, int64_t n, const float* scale_inv,
-                                      void* y, int ydtype, void* stream);
+fp8q_status_t fp8q_dequant_per_tensor(const uint8_t* q, fp8q_fmt_t fmt, int64_t n, const float* scale_inv,
+                                      void* y, fp8q_dtype_t ydtype, void* stream);
 
 /*
  * Per-channel dequant (ColossalAI fp8.py, cast_from_fp8, per_channel_scale=True):
  *   y[r, c] = ydtype(fp32(q[r, c]) * scale_inv[r]); scale_inv has `rows` floats.
  */
-fp8q_status_t fp8q_dequant_per_channel(const uint8_t* q, int fmt, int64_t rows, int64_t cols,
-                                       const float* scale_inv, void* y, int ydtype, void* stream);
+fp8q_status_t fp8q_dequant_per_channel(const uint8_t* q, fp8q_fmt_t fmt, int64_t rows, int64_t cols,
+                                       const float* scale_inv, void* y, fp8q_dtype_t ydtype, void* stream);
 
 /*
  * Per-128-group dequant, the inverse of per_token_cast_to_fp8 (DeepEP
@@ -144,8 +144,8 @@ fp8q_status_t fp8q_dequant_per_channel(const uint8_t* q, int fmt, int64_t rows, 
  *   y[r, c] = ydtype(fp32(q[r, c]) * scale_inv[r, c / 128]).
  * cols % 128 != 0 -> FP8Q_ESHAPE.
  */
-fp8q_status_t fp8q_dequant_per_group128(const uint8_t* q, int fmt, int64_t rows, int64_t cols,
-                                        const float* scale_inv, void* y, int ydtype, void* stream);
+fp8q_status_t fp8q_dequant_per_group128(const uint8_t* q, fp8q_fmt_t fmt, int64_t rows, int64_t cols,
+                                        const float* scale_inv, void* y, fp8q_dtype_t ydtype, void* stream);
 
 /*
  * 128x128 block weight dequant (CSDN "FP8 (8 bits) & FP16 (16 bits)",
@@ -155,8 +155,8 @@ fp8q_status_t fp8q_dequant_per_group128(const uint8_t* q, int fmt, int64_t rows,
  * The page stores the product into a bf16 buffer (the default dtype), which
  * is ydtype = FP8Q_BF16; F32 and F16 outputs are also offered.
  */
-fp8q_status_t fp8q_weight_dequant_block128(const uint8_t* q, int fmt, int64_t M, int64_t N,
-                                           const float* scale_inv, void* y, int ydtype, void* stream);
+fp8q_status_t fp8q_weight_dequant_block128(const uint8_t* q, fp8q_fmt_t fmt, int64_t M, int64_t N,
+                                           const float* scale_inv, void* y, fp8q_dtype_t ydtype, void* stream);
 
 /*
  * Cross-rank global scale, one rank's parts (ColossalAI fp8.py,
@@ -175,10 +175,10 @@ fp8q_status_t fp8q_weight_dequant_block128(const uint8_t* q, int fmt, int64_t M,
  * fp8q_dequant_div_scale: y[i] = ydtype(fp32(q[i]) / scale[0]) -- a division by
  *   the scale, which rounds differently from a product with 1 / scale.
  */
-fp8q_status_t fp8q_amax_guarded(const void* x, int xdtype, int64_t n, float* amax, void* stream);
-fp8q_status_t fp8q_cast_with_amax(const void* x, int xdtype, int64_t n, int fmt, const float* amax, uint8_t* q,
+fp8q_status_t fp8q_amax_guarded(const void* x, fp8q_dtype_t xdtype, int64_t n, float* amax, void* stream);
+fp8q_status_t fp8q_cast_with_amax(const void* x, fp8q_dtype_t xdtype, int64_t n, fp8q_fmt_t fmt, const float* amax, uint8_t* q,
                                   float* scale_out, void* stream);
-fp8q_status_t fp8q_dequant_div_scale(const uint8_t* q, int fmt, int64_t n, const float* scale, void* y, int ydtype,
+fp8q_status_t fp8q_dequant_div_scale(const uint8_t* q, fp8q_fmt_t fmt, int64_t n, const float* scale, void* y, fp8q_dtype_t ydtype,
                                      void* stream);
 
 /*
@@ -196,8 +196,8 @@ fp8q_status_t fp8q_dequant_div_scale(const uint8_t* q, int fmt, int64_t n, const
  * ydtype is the original tensor's type (input_type on the page).  W >= 1.
  * n == 0 is a no-op.
  */
-fp8q_status_t fp8q_dequant_sum(const uint8_t* q, int fmt, int64_t W, int64_t n, const float* scale_inv,
-                               int average, void* y, int ydtype, void* stream);
+fp8q_status_t fp8q_dequant_sum(const uint8_t* q, fp8q_fmt_t fmt, int64_t W, int64_t n, const float* scale_inv,
+                               int average, void* y, fp8q_dtype_t ydtype, void* stream);
 
 /*
  * fp8q_dequant_sum followed by cast_to_fp8 of the sum, per tensor
@@ -208,8 +208,8 @@ fp8q_status_t fp8q_dequant_sum(const uint8_t* q, int fmt, int64_t W, int64_t n, 
  * aligned, caller-owned) during the sum pass, so y is read once more, by the
  * cast pass.  n == 0 writes scale_inv_out[0] = 1.0 (the empty-tensor branch).
  */
-fp8q_status_t fp8q_dequant_sum_requant(const uint8_t* q, int fmt, int64_t W, int64_t n, const float* scale_inv,
-                                       int average, void* y, int ydtype, uint8_t* q_out, float* scale_inv_out,
+fp8q_status_t fp8q_dequant_sum_requant(const uint8_t* q, fp8q_fmt_t fmt, int64_t W, int64_t n, const float* scale_inv,
+                                       int average, void* y, fp8q_dtype_t ydtype, uint8_t* q_out, float* scale_inv_out,
                                        void* workspace, void* stream);
 
 /*
@@ -234,10 +234,10 @@ fp8q_status_t fp8q_dequant_sum_requant(const uint8_t* q, int fmt, int64_t W, int
  *   fp8q_dequant_per_tensor in that format).  A format word other than 0 or 1
  *   (the page raises TypeError) writes NaN to every y.  n == 0 is a no-op.
  */
-fp8q_status_t fp8q_cast_to_fp8_pipeline(const void* x, int xdtype, int64_t n, uint8_t* q, float* scale_inv,
+fp8q_status_t fp8q_cast_to_fp8_pipeline(const void* x, fp8q_dtype_t xdtype, int64_t n, uint8_t* q, float* scale_inv,
                                         int32_t* fmt_out, void* workspace, void* stream);
 fp8q_status_t fp8q_cast_from_fp8_pipeline(const uint8_t* q, const int32_t* fmt, int64_t n, const float* scale_inv,
-                                          void* y, int ydtype, void* stream);
+                                          void* y, fp8q_dtype_t ydtype, void* stream);
 
 /*
  * Packed [scale_inv | payload] slots of the fp8 all-gather (ColossalAI
@@ -258,9 +258,9 @@ fp8q_status_t fp8q_cast_from_fp8_pipeline(const uint8_t* q, const int32_t* fmt, 
  *   W == 1 dequantizes one slot, the ring's per-step cast.  W == 0 or
  *   n == 0 is a no-op.
  */
-fp8q_status_t fp8q_cast_to_packed(const void* x, int xdtype, int64_t n, int fmt, uint8_t* slot, void* workspace,
+fp8q_status_t fp8q_cast_to_packed(const void* x, fp8q_dtype_t xdtype, int64_t n, fp8q_fmt_t fmt, uint8_t* slot, void* workspace,
                                   void* stream);
-fp8q_status_t fp8q_dequant_packed(const uint8_t* slots, int fmt, int64_t W, int64_t n, void* y, int ydtype,
+fp8q_status_t fp8q_dequant_packed(const uint8_t* slots, fp8q_fmt_t fmt, int64_t W, int64_t n, void* y, fp8q_dtype_t ydtype,
                                   void* stream);
 
 #ifdef __cplusplus
