@@ -1,7 +1,19 @@
-"""Helpers for the GPU parity tests: host <-> device marshalling and
-bit-exact comparisons with NaN compared by class (the exact NaN code the
-hardware emits is not fixed by the pages)."""
+"""Helpers for the GPU parity tests: host <-> device marshalling, guarded
+device buffers, and bit-exact comparisons with NaN compared by class (the
+exact NaN code the hardware emits is not fixed by the pages).
+
+Guard canaries: ``G.empty`` / ``G.full`` / ``G.zeros`` / ``G.ones`` allocate
+every device buffer of a test inside a larger one, with GUARD bytes of a fixed
+pattern before and after it.  The conftest fixture calls ``G.check()`` after
+every GPU test: a kernel store past either end of an output (a ragged tail, a
+byte-store path, a grid-stride edge) changes a guard and fails the test, where
+a plain exact-size allocation would hide it.  Buffers above GUARD_LIMIT bytes
+(the beyond-2^32 tests) are allocated plainly so that they can be freed
+mid-test.
+"""
 from __future__ import annotations
+
+import math
 
 import numpy as np
 import torch
@@ -13,13 +25,79 @@ FP8_NAN_CLASS = {
 TORCH_HP = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 
+GUARD = 4096                    # bytes of canary on each side (keeps 4 KiB alignment)
+GUARD_PATTERN = 0xA5
+GUARD_LIMIT = 2 << 30           # larger buffers are not guarded (they are freed mid-test)
+
+
+class GuardedAllocator:
+    """Device buffers with canary regions on both sides (see the module
+    docstring).  The signatures follow torch.empty / torch.full."""
+
+    def __init__(self):
+        self.live = []          # (backing uint8 buffer, payload bytes, shape, dtype)
+
+    @staticmethod
+    def _shape(size):
+        if len(size) == 1 and isinstance(size[0], (tuple, list, torch.Size)):
+            size = tuple(size[0])
+        return tuple(int(d) for d in size)
+
+    def empty(self, *size, dtype=torch.float32, device="cuda:0"):
+        shape = self._shape(size)
+        if torch.device(device).type != "cuda":
+            return torch.empty(shape, dtype=dtype, device=device)
+        nbytes = math.prod(shape) * torch.empty(0, dtype=dtype).element_size()
+        if nbytes > GUARD_LIMIT:
+            return torch.empty(shape, dtype=dtype, device=device)
+        raw = torch.empty(nbytes + 2 * GUARD, dtype=torch.uint8, device=device)
+        raw[:GUARD].fill_(GUARD_PATTERN)
+        raw[GUARD + nbytes:].fill_(GUARD_PATTERN)
+        self.live.append((raw, nbytes, shape, dtype))
+        return raw[GUARD:GUARD + nbytes].view(dtype).view(shape)
+
+    def full(self, size, fill_value, dtype=torch.float32, device="cuda:0"):
+        t = self.empty(size, dtype=dtype, device=device)
+        return t.fill_(fill_value) if t.numel() else t
+
+    def zeros(self, *size, dtype=torch.float32, device="cuda:0"):
+        return self.full(self._shape(size), 0, dtype=dtype, device=device)
+
+    def ones(self, *size, dtype=torch.float32, device="cuda:0"):
+        return self.full(self._shape(size), 1, dtype=dtype, device=device)
+
+    def check(self):
+        """Synchronize, assert every live buffer's canaries are intact, and
+        release them."""
+        live, self.live = self.live, []
+        if not live:
+            return
+        torch.cuda.synchronize()
+        bad = []
+        for raw, nbytes, shape, dtype in live:
+            for side, g in (("before", raw[:GUARD]), ("after", raw[GUARD + nbytes:])):
+                h = g.cpu().numpy()
+                off = np.nonzero(h != GUARD_PATTERN)[0]
+                if off.size:
+                    bad.append(f"{side} {tuple(shape)} {dtype}: {off.size} guard bytes changed, first at "
+                               f"offset {int(off[0]) - (GUARD if side == 'before' else 0)} "
+                               f"from the {'start' if side == 'before' else 'end'} (value {int(h[off[0]]):#04x})")
+        assert not bad, "store outside an output buffer: " + "; ".join(bad)
+
+
+G = GuardedAllocator()
+
+
 def dev(a: np.ndarray, dtype: str = None) -> torch.Tensor:
-    """numpy host array -> contiguous device tensor.  uint16 arrays are
-    reinterpreted as bf16 or f16 by `dtype`."""
+    """numpy host array -> contiguous device tensor (guarded).  uint16 arrays
+    are reinterpreted as bf16 or f16 by `dtype`."""
     t = torch.from_numpy(np.ascontiguousarray(a))
     if dtype in ("bf16", "f16"):
         t = t.view(torch.int16).view(TORCH_HP[dtype])
-    return t.to("cuda:0")
+    out = G.empty(t.shape, dtype=t.dtype)
+    if out.numel():
+        out.copy_(t)
+    return out
 
 
 def host(t: torch.Tensor) -> np.ndarray:
@@ -32,7 +110,7 @@ def host(t: torch.Tensor) -> np.ndarray:
 
 
 def empty_hp(shape, dtype: str) -> torch.Tensor:
-    return torch.empty(shape, dtype=TORCH_HP[dtype], device="cuda:0")
+    return G.empty(shape, dtype=TORCH_HP[dtype], device="cuda:0")
 
 
 def assert_fp8_equal(got: np.ndarray, want: np.ndarray, fmt: str, what: str = ""):

@@ -7,7 +7,7 @@ import torch
 import dequantize_amax_reduce_amd as fq
 import oracle
 from dequantize_amax_reduce_amd import workloads as W
-from gpu_util import assert_f32_equal, assert_fp8_equal, assert_hp_equal, dev, host
+from gpu_util import G, assert_f32_equal, assert_fp8_equal, assert_hp_equal, dev, host
 
 pytestmark = pytest.mark.gpu
 
@@ -28,19 +28,19 @@ def test_cast_to_from_fp8_helpers():
             assert_hp_equal(host(y), deq(wq, tfmt, ws, "bf16"), "bf16")
             # the out= forms write into the caller's tensors and return them;
             # cast_from_fp8 takes out's dtype (fp32 here), as torch.mul(..., out=out) does
-            qo = torch.full(x.shape, 0x55, dtype=torch.uint8, device="cuda:0")
+            qo = G.full(x.shape, 0x55, dtype=torch.uint8, device="cuda:0")
             r, s2 = fq.cast_to_fp8(x, fmt, per_channel_scale=per_channel, out=qo)
             assert r is qo
             assert_fp8_equal(host(qo), wq, tfmt)
             assert_f32_equal(host(s2), ws)
-            yo = torch.full(x.shape, 7.0, dtype=torch.float32, device="cuda:0")
+            yo = G.full(x.shape, 7.0, dtype=torch.float32, device="cuda:0")
             r = fq.cast_from_fp8(q, s, torch.bfloat16, per_channel_scale=per_channel, out=yo)
             assert r is yo
             assert_f32_equal(host(yo), deq(wq, tfmt, ws, "f32"))
     with pytest.raises(TypeError):   # out of the other fp8 format
-        fq.cast_to_fp8(dev(xb, "bf16"), "e4m3", out=torch.empty(xb.shape, dtype=torch.float8_e5m2, device="cuda:0"))
+        fq.cast_to_fp8(dev(xb, "bf16"), "e4m3", out=G.empty(xb.shape, dtype=torch.float8_e5m2, device="cuda:0"))
     with pytest.raises(ValueError):  # out of the wrong size
-        fq.cast_from_fp8(q, s, torch.bfloat16, out=torch.empty(5, dtype=torch.float32, device="cuda:0"))
+        fq.cast_from_fp8(q, s, torch.bfloat16, out=G.empty(5, dtype=torch.float32, device="cuda:0"))
 
 
 def test_per_token_and_weight_dequant_helpers():
@@ -59,14 +59,14 @@ def test_per_token_and_weight_dequant_helpers():
 
 
 def test_errors_surface_as_python_exceptions():
-    x = torch.zeros((4, 100), dtype=torch.bfloat16, device="cuda:0")
+    x = G.zeros((4, 100), dtype=torch.bfloat16, device="cuda:0")
     with pytest.raises(ValueError):
         fq.per_token_cast_to_fp8(x)
     with pytest.raises(TypeError):
-        fq.cast_to_fp8(torch.zeros(4, dtype=torch.int32, device="cuda:0"))
+        fq.cast_to_fp8(G.zeros(4, dtype=torch.int32, device="cuda:0"))
     with pytest.raises(ValueError):
-        fq.fp8q_cast_per_group128(x.t(), torch.empty((100, 4), dtype=torch.uint8, device="cuda:0"),
-                                  torch.empty(0, dtype=torch.float32, device="cuda:0"))
+        fq.fp8q_cast_per_group128(x.t(), G.empty((100, 4), dtype=torch.uint8, device="cuda:0"),
+                                  G.empty(0, dtype=torch.float32, device="cuda:0"))
 
 
 def test_non_default_stream_ordering():

@@ -9,14 +9,14 @@ import torch
 import dequantize_amax_reduce_amd as fq
 import oracle
 from dequantize_amax_reduce_amd import workloads as W
-from gpu_util import assert_hp_equal, dev, empty_hp, host
+from gpu_util import G, assert_hp_equal, dev, empty_hp, host
 
 pytestmark = pytest.mark.gpu
 
 
 def _run(q, s, fmt, ydtype, q_offset=0, y_offset=0):
     M, N = q.shape
-    qb = torch.empty(M * N + q_offset, dtype=torch.uint8, device="cuda:0")
+    qb = G.empty(M * N + q_offset, dtype=torch.uint8, device="cuda:0")
     qb[q_offset:] = dev(q.reshape(-1))
     yb = empty_hp(M * N + y_offset, ydtype)
     y = yb[y_offset:].view(M, N)
@@ -68,8 +68,8 @@ def test_block_dequant_all_codes_extreme_scales():
 
 def test_block_dequant_empty():
     for M, N in [(0, 128), (128, 0)]:
-        q = torch.empty((M, N), dtype=torch.uint8, device="cuda:0")
-        s = torch.empty(((M + 127) // 128, (N + 127) // 128), dtype=torch.float32, device="cuda:0")
-        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+        q = G.empty((M, N), dtype=torch.uint8, device="cuda:0")
+        s = G.empty(((M + 127) // 128, (N + 127) // 128), dtype=torch.float32, device="cuda:0")
+        y = G.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
         fq.fp8q_weight_dequant_block128(q, s, y)
         torch.cuda.synchronize()

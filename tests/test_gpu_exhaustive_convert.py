@@ -13,7 +13,7 @@ import torch
 
 import dequantize_amax_reduce_amd as fq
 import oracle
-from gpu_util import FP8_NAN_CLASS
+from gpu_util import G, FP8_NAN_CLASS
 
 pytestmark = pytest.mark.gpu
 FP8_MAX = {"e4m3fn": 448.0, "e5m2": 57344.0}
@@ -36,8 +36,8 @@ def test_every_binary32_input(fmt):
     assert L is not None
     threads = max(1, min(16, os.cpu_count() or 1))
     amax = torch.tensor([FP8_MAX[fmt]], dtype=torch.float32, device="cuda:0")
-    scale = torch.empty(1, dtype=torch.float32, device="cuda:0")
-    q = torch.empty(CHUNK, dtype=torch.uint8, device="cuda:0")
+    scale = G.empty(1, dtype=torch.float32, device="cuda:0")
+    q = G.empty(CHUNK, dtype=torch.uint8, device="cuda:0")
     with ThreadPoolExecutor(threads) as pool:
         for c0 in range(0, 1 << 32, CHUNK):
             print(f"[case] {fmt} inputs 0x{c0:08X}..0x{c0 + CHUNK - 1:08X}", flush=True)

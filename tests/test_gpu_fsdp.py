@@ -9,7 +9,7 @@ import torch
 import dequantize_amax_reduce_amd as fq
 import oracle
 from dequantize_amax_reduce_amd import workloads as W
-from gpu_util import assert_f32_equal, assert_fp8_equal, assert_hp_equal, dev, empty_hp, host
+from gpu_util import G, assert_f32_equal, assert_fp8_equal, assert_hp_equal, dev, empty_hp, host
 
 pytestmark = pytest.mark.gpu
 
@@ -32,7 +32,7 @@ def test_fsdp_hook_parts(fmt, dtype):
     shards = _shards(dtype, seed=len(dtype) * 3 + len(fmt))
     locs = []
     for sh in shards:
-        a = torch.empty(1, dtype=torch.float32, device="cuda:0")
+        a = G.empty(1, dtype=torch.float32, device="cuda:0")
         print(f"[case] amax_guarded {dtype} n={sh.size}", flush=True)
         fq.fp8q_amax_guarded(dev(sh, dtype), a)
         locs.append(a)
@@ -43,8 +43,8 @@ def test_fsdp_hook_parts(fmt, dtype):
     g = np.float32(max(oracle.amax_guarded(sh, dtype) for sh in shards))
     assert host(gmax)[0] == g
     for sh in shards:
-        q = torch.empty(sh.size, dtype=torch.uint8, device="cuda:0")
-        sc = torch.empty(1, dtype=torch.float32, device="cuda:0")
+        q = G.empty(sh.size, dtype=torch.uint8, device="cuda:0")
+        sc = G.empty(1, dtype=torch.float32, device="cuda:0")
         print(f"[case] cast_with_amax {fmt} {dtype} n={sh.size}", flush=True)
         fq.fp8q_cast_with_amax(dev(sh, dtype), gmax, q, sc, fmt)
         torch.cuda.synchronize()
@@ -65,8 +65,8 @@ def test_cast_with_too_small_amax_saturates():
     x = (rng.standard_normal(5000) * 100).astype(np.float32)
     for fmt in ("e4m3fn", "e5m2"):
         for a in (np.float32(1.0), np.float32(0.0), np.float32(1e-38)):
-            q = torch.empty(x.size, dtype=torch.uint8, device="cuda:0")
-            sc = torch.empty(1, dtype=torch.float32, device="cuda:0")
+            q = G.empty(x.size, dtype=torch.uint8, device="cuda:0")
+            sc = G.empty(1, dtype=torch.float32, device="cuda:0")
             fq.fp8q_cast_with_amax(dev(x), dev(np.array([a], np.float32)), q, sc, fmt)
             torch.cuda.synchronize()
             wq, wsc = oracle.cast_with_amax(x, "f32", fmt, a)
@@ -75,17 +75,17 @@ def test_cast_with_too_small_amax_saturates():
 
 
 def test_guarded_amax_special():
-    z = torch.zeros(100, dtype=torch.bfloat16, device="cuda:0")
-    a = torch.empty(1, dtype=torch.float32, device="cuda:0")
+    z = G.zeros(100, dtype=torch.bfloat16, device="cuda:0")
+    a = G.empty(1, dtype=torch.float32, device="cuda:0")
     fq.fp8q_amax_guarded(z, a)
     torch.cuda.synchronize()
     assert host(a)[0] == 1.0
-    x = torch.ones(100, dtype=torch.float32, device="cuda:0")
+    x = G.ones(100, dtype=torch.float32, device="cuda:0")
     x[7] = float("nan")
     fq.fp8q_amax_guarded(x, a)
     torch.cuda.synchronize()
     assert host(a)[0] == 1.0                          # torch.where(NaN > 0, NaN, 1) = 1
-    fq.fp8q_amax_guarded(torch.empty(0, dtype=torch.float32, device="cuda:0"), a)
+    fq.fp8q_amax_guarded(G.empty(0, dtype=torch.float32, device="cuda:0"), a)
     torch.cuda.synchronize()
     assert host(a)[0] == 1.0
 
@@ -95,10 +95,10 @@ def test_fsdp_full_size_shard():
     guarded amax to e5m2 and dequantized by division back to bf16."""
     x = W.gradient_payload()
     xd = dev(x, "bf16")
-    a = torch.empty(1, dtype=torch.float32, device="cuda:0")
-    q = torch.empty(x.size, dtype=torch.uint8, device="cuda:0")
-    sc = torch.empty(1, dtype=torch.float32, device="cuda:0")
-    y = torch.empty(x.size, dtype=torch.bfloat16, device="cuda:0")
+    a = G.empty(1, dtype=torch.float32, device="cuda:0")
+    q = G.empty(x.size, dtype=torch.uint8, device="cuda:0")
+    sc = G.empty(1, dtype=torch.float32, device="cuda:0")
+    y = G.empty(x.size, dtype=torch.bfloat16, device="cuda:0")
     print("[case] fsdp full-size shard", flush=True)
     fq.fp8q_amax_guarded(xd, a)
     fq.fp8q_cast_with_amax(xd, a, q, sc, "e5m2")

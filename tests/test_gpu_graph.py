@@ -7,7 +7,7 @@ import torch
 
 import dequantize_amax_reduce_amd as fq
 from dequantize_amax_reduce_amd import workloads as W
-from gpu_util import host
+from gpu_util import G, host
 
 import pytest
 
@@ -51,36 +51,36 @@ def test_graph_replays_match_eager():
     R, C = xh.shape
     b = {
         "x": torch.from_numpy(xh).view(torch.int16).view(torch.bfloat16).to(dev),
-        "qg": torch.empty((R, C), dtype=torch.uint8, device=dev),
-        "sg": torch.empty((R, C // 128), dtype=torch.float32, device=dev),
-        "yg": torch.empty((R, C), dtype=torch.bfloat16, device=dev),
-        "qt": torch.empty((R, C), dtype=torch.uint8, device=dev),
-        "st": torch.empty(1, dtype=torch.float32, device=dev),
-        "ws": torch.empty(fq.fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32, device=dev),
-        "yt": torch.empty((R, C), dtype=torch.float32, device=dev),
-        "qc": torch.empty((R, C), dtype=torch.uint8, device=dev),
-        "sc": torch.empty(R, dtype=torch.float32, device=dev),
+        "qg": G.empty((R, C), dtype=torch.uint8, device=dev),
+        "sg": G.empty((R, C // 128), dtype=torch.float32, device=dev),
+        "yg": G.empty((R, C), dtype=torch.bfloat16, device=dev),
+        "qt": G.empty((R, C), dtype=torch.uint8, device=dev),
+        "st": G.empty(1, dtype=torch.float32, device=dev),
+        "ws": G.empty(fq.fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32, device=dev),
+        "yt": G.empty((R, C), dtype=torch.float32, device=dev),
+        "qc": G.empty((R, C), dtype=torch.uint8, device=dev),
+        "sc": G.empty(R, dtype=torch.float32, device=dev),
         "qw": torch.from_numpy(cw).to(dev),
         "sw": torch.from_numpy(sw).to(dev),
-        "yw": torch.empty(cw.shape, dtype=torch.bfloat16, device=dev),
-        "amax": torch.empty(1, dtype=torch.float32, device=dev),
-        "qp": torch.empty((R, C), dtype=torch.uint8, device=dev),
-        "sp": torch.empty(1, dtype=torch.float32, device=dev),
-        "wp": torch.empty(1, dtype=torch.int32, device=dev),
-        "yp": torch.empty((R, C), dtype=torch.bfloat16, device=dev),
-        "pk": torch.empty(2 * (4 + R * C // 2), dtype=torch.uint8, device=dev),
-        "ypk": torch.empty((R, C), dtype=torch.bfloat16, device=dev),
+        "yw": G.empty(cw.shape, dtype=torch.bfloat16, device=dev),
+        "amax": G.empty(1, dtype=torch.float32, device=dev),
+        "qp": G.empty((R, C), dtype=torch.uint8, device=dev),
+        "sp": G.empty(1, dtype=torch.float32, device=dev),
+        "wp": G.empty(1, dtype=torch.int32, device=dev),
+        "yp": G.empty((R, C), dtype=torch.bfloat16, device=dev),
+        "pk": G.empty(2 * (4 + R * C // 2), dtype=torch.uint8, device=dev),
+        "ypk": G.empty((R, C), dtype=torch.bfloat16, device=dev),
         "pk_codes": torch.from_numpy(W.received_chunks(4, R * C // 4, "e5m2", seed=9)[0]).to(dev),
         "pk_sinv": torch.from_numpy(W.received_chunks(4, R * C // 4, "e5m2", seed=9)[1]).to(dev),
-        "ysum": torch.empty(R * C // 4, dtype=torch.bfloat16, device=dev),
-        "yrq": torch.empty(R * C // 4, dtype=torch.bfloat16, device=dev),
-        "qrq": torch.empty(R * C // 4, dtype=torch.uint8, device=dev),
-        "srq": torch.empty(1, dtype=torch.float32, device=dev),
-        "ws2": torch.empty(fq.fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32, device=dev),
-        "amg": torch.empty(1, dtype=torch.float32, device=dev),
-        "qfs": torch.empty((R, C), dtype=torch.uint8, device=dev),
-        "sfs": torch.empty(1, dtype=torch.float32, device=dev),
-        "yfs": torch.empty((R, C), dtype=torch.bfloat16, device=dev),
+        "ysum": G.empty(R * C // 4, dtype=torch.bfloat16, device=dev),
+        "yrq": G.empty(R * C // 4, dtype=torch.bfloat16, device=dev),
+        "qrq": G.empty(R * C // 4, dtype=torch.uint8, device=dev),
+        "srq": G.empty(1, dtype=torch.float32, device=dev),
+        "ws2": G.empty(fq.fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32, device=dev),
+        "amg": G.empty(1, dtype=torch.float32, device=dev),
+        "qfs": G.empty((R, C), dtype=torch.uint8, device=dev),
+        "sfs": G.empty(1, dtype=torch.float32, device=dev),
+        "yfs": G.empty((R, C), dtype=torch.bfloat16, device=dev),
     }
     _run_all(b)                       # eager reference (also warms up every kernel)
     torch.cuda.synchronize()

@@ -12,7 +12,7 @@ import torch
 import dequantize_amax_reduce_amd as fq
 import oracle
 from dequantize_amax_reduce_amd import workloads as W
-from gpu_util import assert_f32_equal, assert_fp8_equal, assert_hp_equal, dev, empty_hp, host
+from gpu_util import G, assert_f32_equal, assert_fp8_equal, assert_hp_equal, dev, empty_hp, host
 
 pytestmark = pytest.mark.gpu
 FMTS = ("e4m3fn", "e5m2")
@@ -24,9 +24,9 @@ def _gpu_group_cast(x_host, dtype, fmt, x_offset=0, q_offset=0):
     rows, cols = x_host.shape
     flat = dev(np.concatenate([np.zeros(x_offset, x_host.dtype), x_host.reshape(-1)]), dtype)
     x = flat[x_offset:].view(rows, cols)
-    qbuf = torch.empty(rows * cols + q_offset, dtype=torch.uint8, device="cuda:0")
+    qbuf = G.empty(rows * cols + q_offset, dtype=torch.uint8, device="cuda:0")
     q = qbuf[q_offset:].view(rows, cols)
-    s = torch.empty((rows, cols // 128), dtype=torch.float32, device="cuda:0")
+    s = G.empty((rows, cols // 128), dtype=torch.float32, device="cuda:0")
     print(f"[case] group128 cast {dtype} {fmt} {rows}x{cols} x_off={x_offset} q_off={q_offset}", flush=True)
     fq.fp8q_cast_per_group128(x, q, s, fmt)
     torch.cuda.synchronize()
@@ -138,8 +138,8 @@ def test_activation_config_full_size():
 
 def test_group_cast_empty():
     for shape in [(0, 128), (5, 0), (0, 0)]:
-        x = torch.empty(shape, dtype=torch.bfloat16, device="cuda:0")
-        q = torch.empty(shape, dtype=torch.uint8, device="cuda:0")
-        s = torch.empty((shape[0], shape[1] // 128), dtype=torch.float32, device="cuda:0")
+        x = G.empty(shape, dtype=torch.bfloat16, device="cuda:0")
+        q = G.empty(shape, dtype=torch.uint8, device="cuda:0")
+        s = G.empty((shape[0], shape[1] // 128), dtype=torch.float32, device="cuda:0")
         fq.fp8q_cast_per_group128(x, q, s)
         torch.cuda.synchronize()

@@ -16,7 +16,7 @@ import torch
 
 import dequantize_amax_reduce_amd as fq
 import oracle
-from gpu_util import assert_f32_equal, assert_fp8_equal, assert_hp_equal, host
+from gpu_util import G, assert_f32_equal, assert_fp8_equal, assert_hp_equal, host
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -49,9 +49,9 @@ def test_group128_beyond_2_31_elements():
     _need(24)
     print(f"[case] group128 [{R}, {C}] ({R * C} elements)", flush=True)
     x = torch.randn((R, C), generator=_gen(81), device=DEV, dtype=torch.float32).to(torch.bfloat16)
-    q = torch.empty((R, C), dtype=torch.uint8, device=DEV)
-    s = torch.empty((R, C // 128), dtype=torch.float32, device=DEV)
-    y = torch.empty((R, C), dtype=torch.bfloat16, device=DEV)
+    q = G.empty((R, C), dtype=torch.uint8, device=DEV)
+    s = G.empty((R, C // 128), dtype=torch.float32, device=DEV)
+    y = G.empty((R, C), dtype=torch.bfloat16, device=DEV)
     fq.fp8q_cast_per_group128(x, q, s, "e4m3fn")
     fq.fp8q_dequant_per_group128(q, s, y)
     torch.cuda.synchronize()
@@ -74,10 +74,10 @@ def test_per_tensor_beyond_2_32_elements():
     print(f"[case] per-tensor bf16 n={n}, maximum at {peak}", flush=True)
     x = torch.randn(n, generator=_gen(83), device=DEV, dtype=torch.bfloat16)
     x[peak] = -300.0                      # |x| of N(0, 1) stays far below 300 over 2^32 draws
-    q = torch.empty(n, dtype=torch.uint8, device=DEV)
-    si = torch.empty(1, dtype=torch.float32, device=DEV)
-    ws = torch.empty(fq.fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32, device=DEV)
-    amax = torch.empty(1, dtype=torch.float32, device=DEV)
+    q = G.empty(n, dtype=torch.uint8, device=DEV)
+    si = G.empty(1, dtype=torch.float32, device=DEV)
+    ws = G.empty(fq.fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32, device=DEV)
+    amax = G.empty(1, dtype=torch.float32, device=DEV)
     fq.fp8q_amax(x, amax)
     fq.fp8q_cast_per_tensor(x, q, si, ws, "e5m2")
     torch.cuda.synchronize()
@@ -94,7 +94,7 @@ def test_per_tensor_beyond_2_32_elements():
     assert_fp8_equal(qs, wq, "e5m2", "sampled q")
     del x
     torch.cuda.empty_cache()
-    y = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    y = G.empty(n, dtype=torch.bfloat16, device=DEV)
     fq.fp8q_dequant_per_tensor(q, si, y, "e5m2")
     torch.cuda.synchronize()
     assert_hp_equal(_bits(y[ti]), oracle.dequant_per_tensor(wq, "e5m2", wsi, "bf16"), "bf16", "sampled y")
@@ -115,7 +115,7 @@ def test_block_dequant_row_strip_path():
     rng = np.random.Generator(np.random.PCG64(86))
     sh = (10.0 ** rng.uniform(-4.0, -1.0, size=(mb, nb))).astype(np.float32)
     s = torch.from_numpy(sh).to(DEV)
-    y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    y = G.empty((M, N), dtype=torch.bfloat16, device=DEV)
     fq.fp8q_weight_dequant_block128(c, s, y, "e4m3fn")
     torch.cuda.synchronize()
     ii = np.concatenate([[0, 0, M - 1, M - 1, M - 19, 127, 128], rng.integers(0, M, 3000)])
@@ -148,7 +148,7 @@ def test_block_dequant_single_row_beyond_2_32_columns(ydt):
     rng = np.random.Generator(np.random.PCG64(88))
     sh = (10.0 ** rng.uniform(-4.0, -1.0, size=(1, nb))).astype(np.float32)
     s = torch.from_numpy(sh).to(DEV)
-    y = torch.empty((M, N), dtype=torch.bfloat16 if ydt == "bf16" else torch.float32, device=DEV)
+    y = G.empty((M, N), dtype=torch.bfloat16 if ydt == "bf16" else torch.float32, device=DEV)
     fq.fp8q_weight_dequant_block128(c, s, y, "e4m3fn")
     torch.cuda.synchronize()
     jj = np.unique(np.concatenate([np.arange(0, 300), np.arange((1 << 32) - 300, (1 << 32) + 300),

@@ -10,13 +10,13 @@ import torch
 import dequantize_amax_reduce_amd as fq
 import oracle
 from dequantize_amax_reduce_amd import workloads as W
-from gpu_util import assert_hp_equal, dev, empty_hp, host
+from gpu_util import G, assert_hp_equal, dev, empty_hp, host
 
 pytestmark = pytest.mark.gpu
 
 
 def _ws():
-    return torch.empty(fq.fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32, device="cuda:0")
+    return G.empty(fq.fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32, device="cuda:0")
 
 
 def _inputs(Wn, n, dtype, seed):
@@ -35,7 +35,7 @@ def _round_trip(xs, dtype, fmt, ydtypes, base_offset=0, what=""):
     Wn, n = len(xs), xs[0].size
     print(f"[case] packed {what} W={Wn} n={n} {dtype}->{fmt} offset={base_offset}", flush=True)
     ws = _ws()
-    big = torch.full((base_offset + Wn * (4 + n),), 0xA5, dtype=torch.uint8, device="cuda:0")
+    big = G.full((base_offset + Wn * (4 + n),), 0xA5, dtype=torch.uint8, device="cuda:0")
     combined = big[base_offset:]
     for r, x in enumerate(xs):
         fq.fp8q_cast_to_packed(dev(x, dtype), combined[r * (4 + n):(r + 1) * (4 + n)], ws, fmt)
@@ -72,16 +72,16 @@ def test_packed_base_offsets():
 
 
 def test_packed_empty_and_errors():
-    slot = torch.full((4,), 0xEE, dtype=torch.uint8, device="cuda:0")
-    fq.fp8q_cast_to_packed(torch.empty(0, dtype=torch.bfloat16, device="cuda:0"), slot, _ws(), "e5m2")
+    slot = G.full((4,), 0xEE, dtype=torch.uint8, device="cuda:0")
+    fq.fp8q_cast_to_packed(G.empty(0, dtype=torch.bfloat16, device="cuda:0"), slot, _ws(), "e5m2")
     torch.cuda.synchronize()
     assert list(host(slot)) == [0x00, 0x00, 0x80, 0x3F]
     y = empty_hp((3, 0), "bf16")
-    fq.fp8q_dequant_packed(torch.zeros(12, dtype=torch.uint8, device="cuda:0"), 3, 0, y, "e5m2")
-    buf = torch.zeros(2 * (4 + 6), dtype=torch.uint8, device="cuda:0")
+    fq.fp8q_dequant_packed(G.zeros(12, dtype=torch.uint8, device="cuda:0"), 3, 0, y, "e5m2")
+    buf = G.zeros(2 * (4 + 6), dtype=torch.uint8, device="cuda:0")
     with pytest.raises(Exception):          # n % 4 != 0 with W > 1: rejected on the host
         fq.fp8q_dequant_packed(buf, 2, 6, empty_hp((2, 6), "bf16"), "e5m2")
-    misaligned = torch.zeros(3 + 4 + 8, dtype=torch.uint8, device="cuda:0")[3:]
+    misaligned = G.zeros(3 + 4 + 8, dtype=torch.uint8, device="cuda:0")[3:]
     with pytest.raises(Exception):          # slot not 4-byte aligned
         fq.fp8q_cast_to_packed(dev(np.ones(8, np.float32)), misaligned[:12], _ws(), "e5m2")
     torch.cuda.synchronize()
@@ -89,7 +89,7 @@ def test_packed_empty_and_errors():
 
 def test_packed_helpers():
     xs = _inputs(4, 3 * 512, "bf16", seed=71)
-    combined = torch.empty(4 * (4 + xs[0].size), dtype=torch.uint8, device="cuda:0")
+    combined = G.empty(4 * (4 + xs[0].size), dtype=torch.uint8, device="cuda:0")
     for r, x in enumerate(xs):
         fq.all_gather_pack(dev(x, "bf16").reshape(3, 512), combined, r, 4, "e5m2")
     out = fq.all_gather_unpack(combined, 4, (3, 512), torch.bfloat16, "e5m2")

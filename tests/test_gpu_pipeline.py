@@ -10,14 +10,14 @@ import torch
 import dequantize_amax_reduce_amd as fq
 import oracle
 from dequantize_amax_reduce_amd import workloads as W
-from gpu_util import assert_f32_equal, assert_fp8_equal, assert_hp_equal, dev, empty_hp, host
+from gpu_util import G, assert_f32_equal, assert_fp8_equal, assert_hp_equal, dev, empty_hp, host
 
 pytestmark = pytest.mark.gpu
 FMT_WORD = {0: "e4m3fn", 1: "e5m2"}
 
 
 def _ws():
-    return torch.empty(fq.fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32, device="cuda:0")
+    return G.empty(fq.fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32, device="cuda:0")
 
 
 def _to_dtype(x32: np.ndarray, dtype: str) -> np.ndarray:
@@ -35,10 +35,10 @@ def _check_pipeline(xh: np.ndarray, dtype: str, what: str, offset: int = 0, ydty
     print(f"[case] pipeline {what} {dtype} n={n} offset={offset}", flush=True)
     buf = dev(np.concatenate([np.zeros(offset, xh.dtype), xh.reshape(-1)]), dtype)
     x = buf[offset:]
-    qbuf = torch.empty(n + offset, dtype=torch.uint8, device="cuda:0")
+    qbuf = G.empty(n + offset, dtype=torch.uint8, device="cuda:0")
     q = qbuf[offset:]
-    si = torch.empty(1, dtype=torch.float32, device="cuda:0")
-    word = torch.full((1,), -5, dtype=torch.int32, device="cuda:0")
+    si = G.empty(1, dtype=torch.float32, device="cuda:0")
+    word = G.full((1,), -5, dtype=torch.int32, device="cuda:0")
     fq.fp8q_cast_to_fp8_pipeline(x, q, si, word, _ws())
     torch.cuda.synchronize()
     wq, wsi, wfmt = oracle.cast_to_fp8_pipeline(xh.reshape(-1), dtype)
@@ -97,10 +97,10 @@ def test_pipeline_degenerate(dtype):
 
 
 def test_pipeline_empty():
-    x = torch.empty(0, dtype=torch.bfloat16, device="cuda:0")
-    q = torch.empty(0, dtype=torch.uint8, device="cuda:0")
-    si = torch.full((1,), 7.0, dtype=torch.float32, device="cuda:0")
-    word = torch.full((1,), 9, dtype=torch.int32, device="cuda:0")
+    x = G.empty(0, dtype=torch.bfloat16, device="cuda:0")
+    q = G.empty(0, dtype=torch.uint8, device="cuda:0")
+    si = G.full((1,), 7.0, dtype=torch.float32, device="cuda:0")
+    word = G.full((1,), 9, dtype=torch.int32, device="cuda:0")
     fq.fp8q_cast_to_fp8_pipeline(x, q, si, word, _ws())
     torch.cuda.synchronize()
     assert host(si)[0] == 1.0 and int(host(word)[0]) == 0
@@ -111,7 +111,7 @@ def test_pipeline_bad_format_word_gives_nan():
     q = dev(W.fp8_codes_finite(10_000, "e4m3fn", seed=65))
     si = dev(np.array([0.5], np.float32))
     for bad in (2, -1, 0x7FFFFFFF):
-        word = torch.full((1,), bad, dtype=torch.int32, device="cuda:0")
+        word = G.full((1,), bad, dtype=torch.int32, device="cuda:0")
         for ydt in ("bf16", "f32", "f16"):
             y = empty_hp(q.numel(), ydt)
             fq.fp8q_cast_from_fp8_pipeline(q, word, si, y)

@@ -9,7 +9,7 @@ import torch
 
 import dequantize_amax_reduce_amd as fq
 import oracle
-from gpu_util import TORCH_HP, assert_f32_equal, assert_fp8_equal, assert_hp_equal, dev, host
+from gpu_util import G, TORCH_HP, assert_f32_equal, assert_fp8_equal, assert_hp_equal, dev, host
 
 pytestmark = pytest.mark.gpu
 DTYPES = ("f32", "bf16", "f16")
@@ -40,7 +40,7 @@ def _placed(h, dtype, off):
 
 def _empty(shape, tdtype, off):
     n = int(np.prod(shape))
-    return torch.empty(n + off, dtype=tdtype, device="cuda:0")[off:].view(shape)
+    return G.empty(n + off, dtype=tdtype, device="cuda:0")[off:].view(shape)
 
 
 def _case(rng):
@@ -56,7 +56,7 @@ def test_random_group128():
         x = _values(rng, (rows, cols), dtype)
         print(f"[case] group128 #{i} {rows}x{cols} {dtype}->{fmt}->{ydt} x_off={xo} q_off={qo}", flush=True)
         q = _empty((rows, cols), torch.uint8, qo)
-        s = torch.empty((rows, cols // 128), dtype=torch.float32, device="cuda:0")
+        s = G.empty((rows, cols // 128), dtype=torch.float32, device="cuda:0")
         fq.fp8q_cast_per_group128(_placed(x, dtype, xo), q, s, fmt)
         y = _empty((rows, cols), TORCH_HP[ydt], xo)
         fq.fp8q_dequant_per_group128(q, s, y, fmt)
@@ -75,8 +75,8 @@ def test_random_tensor_and_channel():
         x = _values(rng, (n,), dtype)
         print(f"[case] per-tensor #{i} n={n} {dtype}->{fmt}->{ydt} x_off={xo} q_off={qo}", flush=True)
         q = _empty((n,), torch.uint8, qo)
-        s = torch.empty(1, dtype=torch.float32, device="cuda:0")
-        ws = torch.empty(fq.fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32, device="cuda:0")
+        s = G.empty(1, dtype=torch.float32, device="cuda:0")
+        ws = G.empty(fq.fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32, device="cuda:0")
         fq.fp8q_cast_per_tensor(_placed(x, dtype, xo), q, s, ws, fmt)
         y = _empty((n,), TORCH_HP[ydt], xo)
         fq.fp8q_dequant_per_tensor(q, s, y, fmt)
@@ -90,7 +90,7 @@ def test_random_tensor_and_channel():
         x = _values(rng, (rows, cols), dtype)
         print(f"[case] per-channel #{i} {rows}x{cols} {dtype}->{fmt}->{ydt} x_off={xo} q_off={qo}", flush=True)
         q = _empty((rows, cols), torch.uint8, qo)
-        s = torch.empty(rows, dtype=torch.float32, device="cuda:0")
+        s = G.empty(rows, dtype=torch.float32, device="cuda:0")
         fq.fp8q_cast_per_channel(_placed(x, dtype, xo), q, s, fmt)
         y = _empty((rows, cols), TORCH_HP[ydt], xo)
         fq.fp8q_dequant_per_channel(q, s, y, fmt)
@@ -126,11 +126,11 @@ def test_random_reduce_step():
         avg, requant = bool(rng.integers(0, 2)), bool(rng.integers(0, 2))
         print(f"[case] reduce #{i} W={Wn} n={n} {fmt}->{ydt} avg={avg} requant={requant} q_off={qo}", flush=True)
         qd = _placed(c, "u8", qo)
-        y = torch.empty(n, dtype=TORCH_HP[ydt], device="cuda:0")
+        y = G.empty(n, dtype=TORCH_HP[ydt], device="cuda:0")
         if requant:
-            qo_t = torch.empty(n, dtype=torch.uint8, device="cuda:0")
-            so = torch.empty(1, dtype=torch.float32, device="cuda:0")
-            ws = torch.empty(fq.fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32, device="cuda:0")
+            qo_t = G.empty(n, dtype=torch.uint8, device="cuda:0")
+            so = G.empty(1, dtype=torch.float32, device="cuda:0")
+            ws = G.empty(fq.fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32, device="cuda:0")
             fq.fp8q_dequant_sum_requant(qd, dev(s), y, qo_t, so, ws, fmt, avg)
         else:
             fq.fp8q_dequant_sum(qd, dev(s), y, fmt, avg)
@@ -153,11 +153,11 @@ def test_random_packed_pipeline_fsdp():
         n = n - n % 4 if Wn > 1 else n
         xs = [_values(rng, (n,), dtype) for _ in range(Wn)]
         print(f"[case] packed #{i} W={Wn} n={n} {dtype}->{fmt}->{ydt}", flush=True)
-        comb = torch.empty(Wn * (4 + n), dtype=torch.uint8, device="cuda:0")
-        ws = torch.empty(fq.fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32, device="cuda:0")
+        comb = G.empty(Wn * (4 + n), dtype=torch.uint8, device="cuda:0")
+        ws = G.empty(fq.fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32, device="cuda:0")
         for r, x in enumerate(xs):
             fq.fp8q_cast_to_packed(_placed(x, dtype, xo), comb[r * (4 + n):(r + 1) * (4 + n)], ws, fmt)
-        y = torch.empty((Wn, n), dtype=TORCH_HP[ydt], device="cuda:0")
+        y = G.empty((Wn, n), dtype=TORCH_HP[ydt], device="cuda:0")
         fq.fp8q_dequant_packed(comb, Wn, n, y, fmt)
         torch.cuda.synchronize()
         want = np.concatenate([oracle.cast_to_packed(x, dtype, fmt) for x in xs])
@@ -167,12 +167,12 @@ def test_random_packed_pipeline_fsdp():
 
         x = xs[0]
         print(f"[case] pipeline/fsdp #{i} n={n} {dtype}->{ydt} x_off={xo}", flush=True)
-        q = torch.empty(n, dtype=torch.uint8, device="cuda:0")
-        si = torch.empty(1, dtype=torch.float32, device="cuda:0")
-        word = torch.empty(1, dtype=torch.int32, device="cuda:0")
+        q = G.empty(n, dtype=torch.uint8, device="cuda:0")
+        si = G.empty(1, dtype=torch.float32, device="cuda:0")
+        word = G.empty(1, dtype=torch.int32, device="cuda:0")
         xd = _placed(x, dtype, xo)
         fq.fp8q_cast_to_fp8_pipeline(xd, q, si, word, ws)
-        yp = torch.empty(n, dtype=TORCH_HP[ydt], device="cuda:0")
+        yp = G.empty(n, dtype=TORCH_HP[ydt], device="cuda:0")
         fq.fp8q_cast_from_fp8_pipeline(q, word, si, yp)
         torch.cuda.synchronize()
         wq, wsi, wf = oracle.cast_to_fp8_pipeline(x, dtype)
@@ -182,10 +182,10 @@ def test_random_packed_pipeline_fsdp():
         assert_hp_equal(host(yp), oracle.cast_from_fp8_pipeline(wq, wf, wsi[0], ydt), ydt, f"#{i} pipeline y")
 
         a = np.float32(10.0 ** rng.uniform(-8, 8)) if rng.random() < 0.8 else np.float32(0.0)
-        qf = torch.empty(n, dtype=torch.uint8, device="cuda:0")
-        sc = torch.empty(1, dtype=torch.float32, device="cuda:0")
+        qf = G.empty(n, dtype=torch.uint8, device="cuda:0")
+        sc = G.empty(1, dtype=torch.float32, device="cuda:0")
         fq.fp8q_cast_with_amax(xd, dev(np.array([a], np.float32)), qf, sc, fmt)
-        yf = torch.empty(n, dtype=TORCH_HP[ydt], device="cuda:0")
+        yf = G.empty(n, dtype=TORCH_HP[ydt], device="cuda:0")
         fq.fp8q_dequant_div_scale(qf, sc, yf, fmt)
         torch.cuda.synchronize()
         wq, wsc = oracle.cast_with_amax(x, dtype, fmt, a)

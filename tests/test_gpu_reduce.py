@@ -9,14 +9,14 @@ import torch
 import dequantize_amax_reduce_amd as fq
 import oracle
 from dequantize_amax_reduce_amd import workloads as W
-from gpu_util import assert_f32_equal, assert_fp8_equal, assert_hp_equal, dev, empty_hp, host
+from gpu_util import G, assert_f32_equal, assert_fp8_equal, assert_hp_equal, dev, empty_hp, host
 
 pytestmark = pytest.mark.gpu
 
 
 def _sum(q, s, fmt, ydtype, average, requant, q_offset=0):
     Wn, n = q.shape
-    qb = torch.empty(Wn * n + q_offset, dtype=torch.uint8, device="cuda:0")
+    qb = G.empty(Wn * n + q_offset, dtype=torch.uint8, device="cuda:0")
     qb[q_offset:] = dev(q.reshape(-1))
     qd = qb[q_offset:].view(Wn, n)
     y = empty_hp(n, ydtype)
@@ -26,9 +26,9 @@ def _sum(q, s, fmt, ydtype, average, requant, q_offset=0):
         fq.fp8q_dequant_sum(qd, dev(s), y, fmt, average)
         torch.cuda.synchronize()
         return host(y), None, None
-    qo = torch.empty(n, dtype=torch.uint8, device="cuda:0")
-    so = torch.full((1,), -3.0, dtype=torch.float32, device="cuda:0")
-    ws = torch.full((fq.fp8q_per_tensor_workspace_bytes() // 4,), 12345, dtype=torch.int32, device="cuda:0")
+    qo = G.empty(n, dtype=torch.uint8, device="cuda:0")
+    so = G.full((1,), -3.0, dtype=torch.float32, device="cuda:0")
+    ws = G.full((fq.fp8q_per_tensor_workspace_bytes() // 4,), 12345, dtype=torch.int32, device="cuda:0")
     fq.fp8q_dequant_sum_requant(qd, dev(s), y, qo, so, ws, fmt, average)
     torch.cuda.synchronize()
     return host(y), host(qo), host(so)
@@ -77,12 +77,12 @@ def test_dequant_sum_special_values():
 
 
 def test_dequant_sum_empty():
-    q = torch.empty((3, 0), dtype=torch.uint8, device="cuda:0")
-    s = torch.ones(3, dtype=torch.float32, device="cuda:0")
-    y = torch.empty(0, dtype=torch.bfloat16, device="cuda:0")
-    qo = torch.empty(0, dtype=torch.uint8, device="cuda:0")
-    so = torch.zeros(1, dtype=torch.float32, device="cuda:0")
-    ws = torch.empty(fq.fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32, device="cuda:0")
+    q = G.empty((3, 0), dtype=torch.uint8, device="cuda:0")
+    s = G.ones(3, dtype=torch.float32, device="cuda:0")
+    y = G.empty(0, dtype=torch.bfloat16, device="cuda:0")
+    qo = G.empty(0, dtype=torch.uint8, device="cuda:0")
+    so = G.zeros(1, dtype=torch.float32, device="cuda:0")
+    ws = G.empty(fq.fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32, device="cuda:0")
     fq.fp8q_dequant_sum(q, s, y, "e5m2")
     fq.fp8q_dequant_sum_requant(q, s, y, qo, so, ws, "e5m2", True)
     torch.cuda.synchronize()

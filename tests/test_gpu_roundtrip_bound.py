@@ -10,7 +10,7 @@ import torch
 
 import dequantize_amax_reduce_amd as fq
 from dequantize_amax_reduce_amd import workloads as W
-from gpu_util import dev
+from gpu_util import G, dev
 
 pytestmark = pytest.mark.gpu
 
@@ -29,9 +29,9 @@ def test_group128_activation_roundtrip_bound():
     xh, _ = W.activation_outlier_channels()
     x = dev(xh, "bf16")
     R, C = x.shape
-    q = torch.empty((R, C), dtype=torch.uint8, device="cuda:0")
-    s = torch.empty((R, C // 128), dtype=torch.float32, device="cuda:0")
-    y = torch.empty((R, C), dtype=torch.float32, device="cuda:0")
+    q = G.empty((R, C), dtype=torch.uint8, device="cuda:0")
+    s = G.empty((R, C // 128), dtype=torch.float32, device="cuda:0")
+    y = G.empty((R, C), dtype=torch.float32, device="cuda:0")
     print("[case] group128 activation round-trip bound", flush=True)
     fq.fp8q_cast_per_group128(x, q, s, "e4m3fn")
     fq.fp8q_dequant_per_group128(q, s, y)
@@ -44,10 +44,10 @@ def test_group128_activation_roundtrip_bound():
 def test_per_tensor_gradient_roundtrip_bound():
     x = dev(W.gradient_payload(), "bf16")
     n = x.numel()
-    q = torch.empty(n, dtype=torch.uint8, device="cuda:0")
-    s = torch.empty(1, dtype=torch.float32, device="cuda:0")
-    ws = torch.empty(fq.fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32, device="cuda:0")
-    y = torch.empty(n, dtype=torch.float32, device="cuda:0")
+    q = G.empty(n, dtype=torch.uint8, device="cuda:0")
+    s = G.empty(1, dtype=torch.float32, device="cuda:0")
+    ws = G.empty(fq.fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32, device="cuda:0")
+    y = G.empty(n, dtype=torch.float32, device="cuda:0")
     print("[case] per-tensor gradient round-trip bound", flush=True)
     fq.fp8q_cast_per_tensor(x, q, s, ws, "e5m2")
     fq.fp8q_dequant_per_tensor(q, s, y, "e5m2")

@@ -8,7 +8,7 @@ import torch
 import dequantize_amax_reduce_amd as fq
 import oracle
 from dequantize_amax_reduce_amd import workloads as W
-from gpu_util import assert_f32_equal, assert_fp8_equal, assert_hp_equal, dev, host
+from gpu_util import G, assert_f32_equal, assert_fp8_equal, assert_hp_equal, dev, host
 
 pytestmark = pytest.mark.gpu
 
@@ -26,13 +26,13 @@ def test_two_streams_interleaved():
     bufs = []
     for x in (xa, xb):
         n = x.size
-        bufs.append(dict(x=dev(x), q=torch.empty(n, dtype=torch.uint8, device="cuda:0"),
-                         s=torch.empty(1, dtype=torch.float32, device="cuda:0"),
-                         y=torch.empty(n, dtype=torch.bfloat16, device="cuda:0"),
-                         ws=torch.empty(fq.fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32,
+        bufs.append(dict(x=dev(x), q=G.empty(n, dtype=torch.uint8, device="cuda:0"),
+                         s=G.empty(1, dtype=torch.float32, device="cuda:0"),
+                         y=G.empty(n, dtype=torch.bfloat16, device="cuda:0"),
+                         ws=G.empty(fq.fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32,
                                         device="cuda:0"),
-                         g=dev(ga, "bf16"), gq=torch.empty(ga.shape, dtype=torch.uint8, device="cuda:0"),
-                         gs=torch.empty((ga.shape[0], ga.shape[1] // 128), dtype=torch.float32, device="cuda:0")))
+                         g=dev(ga, "bf16"), gq=G.empty(ga.shape, dtype=torch.uint8, device="cuda:0"),
+                         gs=G.empty((ga.shape[0], ga.shape[1] // 128), dtype=torch.float32, device="cuda:0")))
     torch.cuda.synchronize()
     print("[case] two streams, 6 interleaved rounds", flush=True)
     for _ in range(6):
@@ -66,12 +66,12 @@ def test_host_threads_concurrent():
     bufs = []
     for x in xs:
         n = x.size
-        bufs.append(dict(st=torch.cuda.Stream(), x=dev(x), q=torch.empty(n, dtype=torch.uint8, device="cuda:0"),
-                         s=torch.empty(1, dtype=torch.float32, device="cuda:0"),
-                         y=torch.empty(n, dtype=torch.float32, device="cuda:0"),
-                         qc=torch.empty(x.shape, dtype=torch.uint8, device="cuda:0"),
-                         sc=torch.empty(x.shape[0], dtype=torch.float32, device="cuda:0"),
-                         ws=torch.empty(fq.fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32,
+        bufs.append(dict(st=torch.cuda.Stream(), x=dev(x), q=G.empty(n, dtype=torch.uint8, device="cuda:0"),
+                         s=G.empty(1, dtype=torch.float32, device="cuda:0"),
+                         y=G.empty(n, dtype=torch.float32, device="cuda:0"),
+                         qc=G.empty(x.shape, dtype=torch.uint8, device="cuda:0"),
+                         sc=G.empty(x.shape[0], dtype=torch.float32, device="cuda:0"),
+                         ws=G.empty(fq.fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32,
                                         device="cuda:0")))
     torch.cuda.synchronize()
 

@@ -12,7 +12,7 @@ import torch
 import dequantize_amax_reduce_amd as fq
 import oracle
 from dequantize_amax_reduce_amd import workloads as W
-from gpu_util import assert_f32_equal, assert_fp8_equal, assert_hp_equal, dev, empty_hp, host
+from gpu_util import G, assert_f32_equal, assert_fp8_equal, assert_hp_equal, dev, empty_hp, host
 
 pytestmark = pytest.mark.gpu
 FMTS = ("e4m3fn", "e5m2")
@@ -23,9 +23,9 @@ def _tensor_cast(xh, dtype, fmt, x_offset=0):
     n = xh.size
     flat = dev(np.concatenate([np.zeros(x_offset, xh.dtype), xh.reshape(-1)]), dtype)
     x = flat[x_offset:]
-    q = torch.empty(n, dtype=torch.uint8, device="cuda:0")
-    s = torch.empty(1, dtype=torch.float32, device="cuda:0")
-    ws = torch.empty(fq.fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32, device="cuda:0")
+    q = G.empty(n, dtype=torch.uint8, device="cuda:0")
+    s = G.empty(1, dtype=torch.float32, device="cuda:0")
+    ws = G.empty(fq.fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32, device="cuda:0")
     print(f"[case] per-tensor cast {dtype} {fmt} n={n} x_off={x_offset}", flush=True)
     fq.fp8q_cast_per_tensor(x, q, s, ws, fmt)
     torch.cuda.synchronize()
@@ -34,8 +34,8 @@ def _tensor_cast(xh, dtype, fmt, x_offset=0):
 
 def _channel_cast(xh, dtype, fmt):
     rows, cols = xh.shape
-    q = torch.empty((rows, cols), dtype=torch.uint8, device="cuda:0")
-    s = torch.empty(rows, dtype=torch.float32, device="cuda:0")
+    q = G.empty((rows, cols), dtype=torch.uint8, device="cuda:0")
+    s = G.empty(rows, dtype=torch.float32, device="cuda:0")
     print(f"[case] per-channel cast {dtype} {fmt} {rows}x{cols}", flush=True)
     fq.fp8q_cast_per_channel(dev(xh, dtype), q, s, fmt)
     torch.cuda.synchronize()
@@ -120,17 +120,17 @@ def test_amax_entry_point():
         rng = np.random.Generator(np.random.PCG64(n))
         x = rng.standard_normal(n, dtype=np.float32)
         xh = W.to_bf16_bits(x) if dtype == "bf16" else (x.astype(np.float16).view(np.uint16) if dtype == "f16" else x)
-        a = torch.full((1,), -1.0, dtype=torch.float32, device="cuda:0")
+        a = G.full((1,), -1.0, dtype=torch.float32, device="cuda:0")
         fq.fp8q_amax(dev(xh, dtype), a)
         torch.cuda.synchronize()
         assert host(a)[0].view(np.uint32) == np.float32(oracle.amax(xh, dtype)).view(np.uint32)
     x = np.ones(1000, np.float32)
     x[500] = np.nan
-    a = torch.zeros(1, dtype=torch.float32, device="cuda:0")
+    a = G.zeros(1, dtype=torch.float32, device="cuda:0")
     fq.fp8q_amax(dev(x), a)
     torch.cuda.synchronize()
     assert np.isnan(host(a)[0])
-    fq.fp8q_amax(torch.empty(0, dtype=torch.float32, device="cuda:0"), a)
+    fq.fp8q_amax(G.empty(0, dtype=torch.float32, device="cuda:0"), a)
     torch.cuda.synchronize()
     assert host(a)[0] == 0.0
 
@@ -188,15 +188,15 @@ def test_gradient_payload_full_size():
     """bf16 [2^28] ~ N(0, 1e-3^2): global amax -> e5m2 cast -> dequant to fp32."""
     x = W.gradient_payload()
     xd = dev(x, "bf16")
-    a = torch.zeros(1, dtype=torch.float32, device="cuda:0")
+    a = G.zeros(1, dtype=torch.float32, device="cuda:0")
     print("[case] gradient payload amax", flush=True)
     fq.fp8q_amax(xd, a)
-    q = torch.empty(x.size, dtype=torch.uint8, device="cuda:0")
-    s = torch.empty(1, dtype=torch.float32, device="cuda:0")
-    ws = torch.empty(fq.fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32, device="cuda:0")
+    q = G.empty(x.size, dtype=torch.uint8, device="cuda:0")
+    s = G.empty(1, dtype=torch.float32, device="cuda:0")
+    ws = G.empty(fq.fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32, device="cuda:0")
     print("[case] gradient payload cast", flush=True)
     fq.fp8q_cast_per_tensor(xd, q, s, ws, "e5m2")
-    y = torch.empty(x.size, dtype=torch.float32, device="cuda:0")
+    y = G.empty(x.size, dtype=torch.float32, device="cuda:0")
     print("[case] gradient payload dequant", flush=True)
     fq.fp8q_dequant_per_tensor(q, s, y, "e5m2")
     torch.cuda.synchronize()
@@ -213,20 +213,20 @@ def test_gradient_payload_full_size():
 
 def test_empty_tensors():
     for fmt in FMTS:
-        x = torch.empty(0, dtype=torch.float32, device="cuda:0")
-        q = torch.empty(0, dtype=torch.uint8, device="cuda:0")
-        s = torch.full((1,), -7.0, dtype=torch.float32, device="cuda:0")
-        ws = torch.empty(fq.fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32, device="cuda:0")
+        x = G.empty(0, dtype=torch.float32, device="cuda:0")
+        q = G.empty(0, dtype=torch.uint8, device="cuda:0")
+        s = G.full((1,), -7.0, dtype=torch.float32, device="cuda:0")
+        ws = G.empty(fq.fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32, device="cuda:0")
         fq.fp8q_cast_per_tensor(x, q, s, ws, fmt)
         torch.cuda.synchronize()
         assert host(s)[0] == 1.0                           # cast_to_fp8's empty branch
-        x2 = torch.empty((4096, 0), dtype=torch.bfloat16, device="cuda:0")
-        q2 = torch.empty((4096, 0), dtype=torch.uint8, device="cuda:0")
-        s2 = torch.full((4096,), -7.0, dtype=torch.float32, device="cuda:0")
+        x2 = G.empty((4096, 0), dtype=torch.bfloat16, device="cuda:0")
+        q2 = G.empty((4096, 0), dtype=torch.uint8, device="cuda:0")
+        s2 = G.full((4096,), -7.0, dtype=torch.float32, device="cuda:0")
         fq.fp8q_cast_per_channel(x2, q2, s2, fmt)
         torch.cuda.synchronize()
         assert np.all(host(s2) == 1.0)
-        x3 = torch.empty((0, 4096), dtype=torch.bfloat16, device="cuda:0")
-        fq.fp8q_cast_per_channel(x3, torch.empty((0, 4096), dtype=torch.uint8, device="cuda:0"),
-                                 torch.empty(0, dtype=torch.float32, device="cuda:0"), fmt)
+        x3 = G.empty((0, 4096), dtype=torch.bfloat16, device="cuda:0")
+        fq.fp8q_cast_per_channel(x3, G.empty((0, 4096), dtype=torch.uint8, device="cuda:0"),
+                                 G.empty(0, dtype=torch.float32, device="cuda:0"), fmt)
         torch.cuda.synchronize()
