@@ -38,11 +38,12 @@ _FP8_DTYPE = {E4M3FN: torch.float8_e4m3fn, E5M2: torch.float8_e5m2}
 _DT = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
 
 
-def _load():
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python dequantize_amax_reduce_amd/build.py` "
+def _load(path: str = LIB_PATH):
+    """ctypes handle of a build of the C ABI with every signature set."""
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python dequantize_amax_reduce_amd/build.py` "
                           "(the HIP library is required; there is no fallback)")
-    L = ctypes.CDLL(LIB_PATH)
+    L = ctypes.CDLL(path)
     P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     sigs = {
         "fp8q_abi_version": (I, []),

@@ -3,6 +3,7 @@ exports every function include/fp8q.h declares, and every argument error is
 reported before any HIP call (these calls enqueue nothing, so they need no
 GPU).  Fake device addresses are never dereferenced on these paths."""
 import ctypes
+import os
 import re
 import subprocess
 
@@ -10,7 +11,12 @@ import pytest
 
 import dequantize_amax_reduce_amd as fq
 
-L = fq.lib
+# test_sanitizers.py reruns this file against the ABI layer built with
+# -fsanitize=address,undefined over host-only launcher stubs
+# (tests/sanitize/fp8q_launch_stubs.cpp); FP8Q_ABI_LIB names that build.
+LIB_PATH = os.environ.get("FP8Q_ABI_LIB") or fq.LIB_PATH
+L = fq._load(LIB_PATH) if LIB_PATH != fq.LIB_PATH else fq.lib
+STUBS = hasattr(L, "fp8q_stub_count")
 P = lambda a: ctypes.c_void_p(a)          # a fake, never-dereferenced address
 A = 0x7F0000000000                          # 256-B aligned fake base
 E4, E5, F32, BF16, F16 = 0, 1, 0, 1, 2
@@ -19,7 +25,7 @@ E4, E5, F32, BF16, F16 = 0, 1, 0, 1, 2
 def test_exports_match_header():
     declared = fq.header_functions()
     assert set(declared) == set(fq.ABI_FUNCTIONS)
-    out = subprocess.run(["nm", "-D", "--defined-only", fq.LIB_PATH], capture_output=True, text=True,
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
     exported = set(re.findall(r" T (fp8q_\w+)$", out, re.M))
     assert set(declared) <= exported, set(declared) - exported
@@ -196,3 +202,47 @@ def test_python_binding_rejects_host_tensors():
         fq.fp8q_cast_per_group128(x, torch.empty((2, 128), dtype=torch.uint8), torch.empty((2, 1)))
     with pytest.raises(TypeError):
         fq.cast_from_fp8(torch.zeros(4), torch.ones(1), torch.float32)
+
+
+@pytest.mark.skipif(not STUBS, reason="needs the launcher-stub build of the ABI layer (run by test_sanitizers.py)")
+def test_valid_calls_reach_the_launchers():
+    """Valid arguments get past validation and reach exactly the launchers
+    each entry point is documented to use; the no-op shapes reach none."""
+    L.fp8q_stub_count.restype = ctypes.c_long
+    L.fp8q_stub_count.argtypes = [ctypes.c_char_p]
+
+    def calls(fn, *args):
+        L.fp8q_stub_reset()
+        assert fn(*args) == fq.OK, fn.__name__
+        names = ("fill_f32", "amax", "amax_partials", "guard_amax", "cast_given_amax", "dequant_packed",
+                 "pipeline_cast", "dequant_pipeline", "tensor_cast", "channel_cast", "group128_cast",
+                 "dequant_flat", "dequant_rows", "block128", "dequant_sum")
+        return {k: L.fp8q_stub_count(k.encode()) for k in names if L.fp8q_stub_count(k.encode())}
+
+    x, q, s, y, ws, w = P(A), P(A + (1 << 20)), P(A + (2 << 20)), P(A + (3 << 20)), P(A + (4 << 20)), P(A + (5 << 20))
+    assert calls(L.fp8q_cast_per_group128, x, BF16, 4, 256, E4, q, s, None) == {"group128_cast": 1}
+    assert calls(L.fp8q_cast_per_group128, None, BF16, 0, 256, E4, None, None, None) == {}
+    assert calls(L.fp8q_cast_per_tensor, x, F32, 16, E5, q, s, ws, None) == {"amax_partials": 1, "tensor_cast": 1}
+    assert calls(L.fp8q_cast_per_tensor, None, F32, 0, E5, None, s, ws, None) == {"fill_f32": 1}
+    assert calls(L.fp8q_cast_per_channel, x, F16, 4, 16, E4, q, s, None) == {"channel_cast": 1}
+    assert calls(L.fp8q_cast_per_channel, None, F16, 4, 0, E4, None, s, None) == {"fill_f32": 1}
+    assert calls(L.fp8q_dequant_per_tensor, q, E4, 16, s, y, BF16, None) == {"dequant_flat": 1}
+    assert calls(L.fp8q_dequant_per_channel, q, E4, 4, 16, s, y, F32, None) == {"dequant_rows": 1}
+    assert calls(L.fp8q_dequant_per_group128, q, E5, 2, 256, s, y, F16, None) == {"dequant_flat": 1}
+    assert calls(L.fp8q_weight_dequant_block128, q, E4, 300, 272, s, y, BF16, None) == {"block128": 1}
+    assert calls(L.fp8q_weight_dequant_block128, None, E4, 0, 272, None, None, BF16, None) == {}
+    assert calls(L.fp8q_amax, x, BF16, 0, s, None) == {"amax": 1}
+    assert calls(L.fp8q_amax_guarded, x, BF16, 10, s, None) == {"amax": 1, "guard_amax": 1}
+    assert calls(L.fp8q_cast_with_amax, None, BF16, 0, E5, w, None, s, None) == {"cast_given_amax": 1}
+    assert calls(L.fp8q_dequant_div_scale, q, E5, 16, s, y, BF16, None) == {"dequant_flat": 1}
+    assert calls(L.fp8q_cast_to_fp8_pipeline, None, BF16, 0, None, s, w, ws, None) == \
+        {"amax_partials": 1, "pipeline_cast": 1}
+    assert calls(L.fp8q_cast_from_fp8_pipeline, q, w, 16, s, y, F32, None) == {"dequant_pipeline": 1}
+    assert calls(L.fp8q_cast_to_packed, x, BF16, 16, E5, q, ws, None) == {"amax_partials": 1, "tensor_cast": 1}
+    assert calls(L.fp8q_cast_to_packed, None, BF16, 0, E5, q, ws, None) == {"fill_f32": 1}
+    assert calls(L.fp8q_dequant_packed, q, E5, 3, 16, y, BF16, None) == {"dequant_packed": 1}
+    assert calls(L.fp8q_dequant_sum, q, E5, 4, 64, s, 1, y, BF16, None) == {"dequant_sum": 1}
+    assert calls(L.fp8q_dequant_sum_requant, q, E5, 4, 64, s, 1, y, BF16, w, P(A + (6 << 20)), ws, None) == \
+        {"dequant_sum": 1, "tensor_cast": 1}
+    assert calls(L.fp8q_dequant_sum_requant, None, E5, 4, 0, s, 1, None, BF16, None, w, ws, None) == \
+        {"fill_f32": 1}
