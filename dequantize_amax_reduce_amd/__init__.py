@@ -51,6 +51,7 @@ def _load(path: str = LIB_PATH):
         "fp8q_per_tensor_workspace_bytes": (ctypes.c_size_t, []),
         "fp8q_amax": (I, [P, I, I64, P, P]),
         "fp8q_cast_per_tensor": (I, [P, I, I64, I, P, P, P, P]),
+        "fp8q_cast_per_tensor_noalloc": (I, [P, I, I64, I, P, P, P]),
         "fp8q_cast_per_channel": (I, [P, I, I64, I64, I, P, P, P]),
         "fp8q_cast_per_group128": (I, [P, I, I64, I64, I, P, P, P]),
         "fp8q_dequant_per_tensor": (I, [P, I, I64, P, P, I, P]),
@@ -81,7 +82,7 @@ ABI_FUNCTIONS = ("fp8q_abi_version", "fp8q_status_str", "fp8q_per_tensor_workspa
                  "fp8q_weight_dequant_block128", "fp8q_dequant_sum", "fp8q_dequant_sum_requant",
                  "fp8q_amax_guarded", "fp8q_cast_with_amax", "fp8q_dequant_div_scale",
                  "fp8q_cast_to_fp8_pipeline", "fp8q_cast_from_fp8_pipeline", "fp8q_cast_to_packed",
-                 "fp8q_dequant_packed")
+                 "fp8q_dequant_packed", "fp8q_cast_per_tensor_noalloc")
 
 
 def header_functions() -> list:
@@ -193,6 +194,18 @@ def fp8q_cast_per_tensor(x, q, scale_inv, workspace, fmt="e4m3fn", stream=None) 
     _check(lib.fp8q_cast_per_tensor(_dev(x, "x"), _hp_dtype(x, "x"), x.numel(), f, _dev(q, "q"),
                                     _dev(scale_inv, "scale_inv"), _dev(workspace, "workspace"),
                                     _stream(x, stream)), "fp8q_cast_per_tensor")
+
+
+def fp8q_cast_per_tensor_noalloc(x, q, scale_inv, fmt="e4m3fn", stream=None) -> None:
+    """fp8q_cast_per_tensor with the library's own device scratch instead of
+    a caller workspace; it allocates nothing.  Calls that overlap in time on
+    one GPU share that scratch and race."""
+    f = _fp8(q, fmt, "q")
+    if q.numel() != x.numel() or scale_inv.dtype != torch.float32 or scale_inv.numel() < 1:
+        raise ValueError("fp8q_cast_per_tensor_noalloc: q must match x and scale_inv must be float32[1]")
+    _check(lib.fp8q_cast_per_tensor_noalloc(_dev(x, "x"), _hp_dtype(x, "x"), x.numel(), f, _dev(q, "q"),
+                                            _dev(scale_inv, "scale_inv"), _stream(x, stream)),
+           "fp8q_cast_per_tensor_noalloc")
 
 
 def fp8q_cast_per_channel(x, q, scale_inv, fmt="e4m3fn", stream=None) -> None:

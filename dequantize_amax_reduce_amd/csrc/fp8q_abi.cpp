@@ -224,6 +224,27 @@ fp8q_status_t fp8q_cast_per_tensor(const void* x, fp8q_dtype_t xdtype, int64_t n
     return launched();
 }
 
+fp8q_status_t fp8q_cast_per_tensor_noalloc(const void* x, fp8q_dtype_t xdtype, int64_t n, fp8q_fmt_t fmt, uint8_t* q,
+                                           float* scale_inv, void* stream) {
+    static_assert(fp8q::kAmaxPartials <= fp8q::kScratchWords, "the amax pass must fit the library scratch");
+    if (n < 0) return FP8Q_EINVAL;
+    int64_t nn;
+    fp8q_status_t st = check_2d(x, xdtype, 1, n, fmt, q, scale_inv, 1, &nn);
+    if (st != FP8Q_OK) return st;
+    if (n == 0) {  // cast_to_fp8's empty-tensor branch: scale_inv = [1.0]
+        fp8q::launch_fill_f32(scale_inv, 1, 1.0f, S(stream));
+        return launched();
+    }
+    // the amax pass's grid is capped, so this holds for every n; checked
+    // before anything is enqueued all the same
+    if (fp8q::amax_partials_count(x, xdtype, n) > fp8q::kScratchWords) return FP8Q_EINVAL;
+    uint32_t* partial = nullptr;
+    if (fp8q::scratch_words(S(stream), &partial) != hipSuccess) return FP8Q_EHIP;
+    const int np = fp8q::launch_amax_partials(x, xdtype, n, partial, S(stream));
+    fp8q::launch_tensor_cast(x, xdtype, n, fmt, partial, np, 1, q, scale_inv, S(stream));
+    return launched();
+}
+
 fp8q_status_t fp8q_cast_per_channel(const void* x, fp8q_dtype_t xdtype, int64_t rows, int64_t cols, fp8q_fmt_t fmt, uint8_t* q,
                                     float* scale_inv, void* stream) {
     int64_t n;

@@ -15,6 +15,8 @@
 // XCDs; in the two-pass casts each workgroup stores one partial, and every
 // workgroup of the cast pass folds all of them.
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "fp8q_device.h"
 
@@ -150,17 +152,16 @@ template <int DT> void run_amax(const void* x, int64_t n, uint32_t* word, hipStr
 // bf16 [4096, 4096]: 20.5 us against 26.9 us with non-temporal loads).
 // Two launches instead of four (slot clear, atomics, slot fold): the bf16
 // [4096, 4096] cast takes 16.4 us against 20.8 us, fp32 28.5 against 31.9.
-template <int DT> int run_amax_partials(const void* x, int64_t n, uint32_t* partial, hipStream_t st) {
+template <int DT> int amax_partials_grid(const void* x, int64_t n) {
     constexpr int VE = LaneVE<DT>::value;
-    const int64_t cap = kAmaxGrid;
-    if (al(x, 16)) {
-        const int64_t chunks = (n / VE + kAmaxK * 256 - 1) / (kAmaxK * 256);
-        const int g = (int)std::min(std::max<int64_t>(chunks, 1), cap);
-        k_amax<DT, true, kAmaxK, false, true><<<g, kThreads, 0, st>>>(x, n, partial, 0);
-        return g;
-    }
-    const int g = (int)std::min(std::max<int64_t>((n + 255) / 256, 1), cap);
-    k_amax<DT, false, kAmaxK, false, true><<<g, kThreads, 0, st>>>(x, n, partial, 0);
+    const int64_t units = al(x, 16) ? (n / VE + kAmaxK * 256 - 1) / (kAmaxK * 256) : (n + 255) / 256;
+    return (int)std::min(std::max<int64_t>(units, 1), kAmaxGrid);
+}
+
+template <int DT> int run_amax_partials(const void* x, int64_t n, uint32_t* partial, hipStream_t st) {
+    const int g = amax_partials_grid<DT>(x, n);
+    if (al(x, 16)) k_amax<DT, true, kAmaxK, false, true><<<g, kThreads, 0, st>>>(x, n, partial, 0);
+    else k_amax<DT, false, kAmaxK, false, true><<<g, kThreads, 0, st>>>(x, n, partial, 0);
     return g;
 }
 
@@ -276,6 +277,58 @@ template <int FMT, int YDT> struct RunDequantSum {
 void launch_dequant_sum(const uint8_t* q, int fmt, int64_t W, int64_t n, const float* sinv, int average, void* y,
                         int ydt, uint32_t* ws, hipStream_t st) {
     dispatch_fmt_ydt<RunDequantSum>(fmt, ydt, q, W, n, sinv, average, y, ws, st);
+}
+
+int amax_partials_count(const void* x, int dt, int64_t n) {
+    if (dt == kF32) return amax_partials_grid<kF32>(x, n);
+    if (dt == kBF16) return amax_partials_grid<kBF16>(x, n);
+    return amax_partials_grid<kF16>(x, n);
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free per-tensor cast (the amax partials), in
+// device memory the library holds: every GPU the library runs on gets its own
+// copy of this array when the code object loads, kept until the process
+// ends.  On the host, `scratch` is only a stand-in symbol: its device address
+// on each GPU comes from hipGetSymbolAddress, looked up once per device with
+// that device current, and only that address is handed to kernels.  Calls
+// that overlap on one GPU share the array and race.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint32_t scratch[kScratchWords];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+std::atomic<uint32_t*> g_scratch_addr[kMaxDevices];
+}  // namespace
+
+hipError_t scratch_words(hipStream_t st, uint32_t** out) {
+    int dev = -1;
+    hipError_t e = st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    uint32_t* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            int cur = -1;
+            if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+            if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+            void* a = nullptr;
+            e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+            if (cur != dev) {
+                const hipError_t e2 = hipSetDevice(cur);
+                if (e == hipSuccess) e = e2;
+            }
+            if (e != hipSuccess) return e;
+            if (a == nullptr) return hipErrorInvalidSymbol;
+            p = (uint32_t*)a;
+            g_scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return hipSuccess;
 }
 
 void launch_fill_f32(float* p, int64_t n, float v, hipStream_t st) {

@@ -27,6 +27,15 @@ void launch_amax(const void* x, int dt, int64_t n, uint32_t* word, hipStream_t s
 // the amax pass of a two-pass cast: stores one partial max |x| per workgroup
 // to partial[0 .. np) and returns np (1 <= np <= kAmaxPartials); n may be 0
 int launch_amax_partials(const void* x, int dt, int64_t n, uint32_t* partial, hipStream_t st);
+// the np that launch_amax_partials(x, dt, n, ...) would use, without launching
+int amax_partials_count(const void* x, int dt, int64_t n);
+// Library-held scratch of the allocation-free per-tensor cast: kScratchWords
+// words (the amax pass's partials) in a __device__ array, one copy per GPU.
+// scratch_words stores the device address of the copy on `st`'s device
+// (taken with hipGetSymbolAddress on the first call per device, with that
+// device current) and returns the HIP error of that lookup.
+constexpr int kScratchWords = kAmaxPartials;
+hipError_t scratch_words(hipStream_t st, uint32_t** out);
 // where(amax > 0, amax, 1) applied to ws[0]
 void launch_guard_amax(uint32_t* ws, hipStream_t st);
 // cast with scale = fp8_max / amax[0] (caller-supplied amax); scale_out[0] = scale

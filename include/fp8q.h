@@ -98,6 +98,25 @@ fp8q_status_t fp8q_cast_per_tensor(const void* x, fp8q_dtype_t xdtype, int64_t n
                                    uint8_t* q, float* scale_inv, void* workspace, void* stream);
 
 /*
+ * fp8q_cast_per_tensor without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same numerics, passes and outputs as
+ * fp8q_cast_per_tensor; it allocates nothing.  The amax partials go to a
+ * scratch array the library holds in device memory: 4096 bytes (1024 words)
+ * per GPU, created with the code object on each GPU the library runs on and
+ * kept until the process ends.  The amax pass never needs more than that,
+ * whatever n is, so every n accepted by fp8q_cast_per_tensor is accepted
+ * here (FP8Q_EINVAL would report a grid that needed more, before anything is
+ * enqueued).  The scratch used is the one on `stream`'s device (the current
+ * device for a NULL stream); its address is looked up on the first call per
+ * device (FP8Q_EHIP if that lookup fails).  Every call on one GPU shares that
+ * GPU's scratch: calls that overlap in time on one GPU (other streams, other
+ * threads) race and give wrong results; calls ordered on one stream are safe.
+ */
+fp8q_status_t fp8q_cast_per_tensor_noalloc(const void* x, fp8q_dtype_t xdtype, int64_t n, fp8q_fmt_t fmt,
+                                           uint8_t* q, float* scale_inv, void* stream);
+
+/*
  * Per-channel cast (ColossalAI fp8.py, cast_to_fp8 with per_channel_scale=True;
  * the channel is the last dimension, so one row of x [rows, cols]).
  *   amax_r = max_c |x[r, c]|; a_r = amax_r > 0 ? amax_r : 1;

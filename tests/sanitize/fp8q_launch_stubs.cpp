@@ -21,7 +21,8 @@ struct Count {
 Count g_counts[] = {{"fill_f32", 0},         {"amax", 0},          {"amax_partials", 0}, {"guard_amax", 0},
                     {"cast_given_amax", 0},  {"dequant_packed", 0}, {"pipeline_cast", 0}, {"dequant_pipeline", 0},
                     {"tensor_cast", 0},      {"channel_cast", 0},  {"group128_cast", 0}, {"dequant_flat", 0},
-                    {"dequant_rows", 0},     {"block128", 0},      {"dequant_sum", 0}};
+                    {"dequant_rows", 0},     {"block128", 0},      {"dequant_sum", 0},
+                    {"scratch_words", 0}};
 
 void hit(const char* name) {
     for (Count& c : g_counts)
@@ -64,6 +65,21 @@ int launch_amax_partials(const void* x, int dt, int64_t n, uint32_t* partial, hi
     need(partial && dt_ok(dt) && n >= 0 && (n == 0 || x));
     hit("amax_partials");
     return 1;
+}
+
+int amax_partials_count(const void* x, int dt, int64_t n) {
+    need(dt_ok(dt) && n >= 0 && (n == 0 || x));
+    return 1;
+}
+
+// a host array stands in for the device scratch: the stubs never dereference it
+uint32_t g_scratch_stub[kScratchWords];
+
+hipError_t scratch_words(hipStream_t, uint32_t** out) {
+    need(out != nullptr);
+    hit("scratch_words");
+    *out = g_scratch_stub;
+    return hipSuccess;
 }
 
 void launch_guard_amax(uint32_t* ws, hipStream_t) { need(ws != nullptr); hit("guard_amax"); }

@@ -65,6 +65,16 @@ def test_tensor_and_channel_errors():
     assert t(P(A), BF16, 16, E4, P(A + 4096), P(A + 8192), P(A + 8192), None) == fq.EINVAL  # ws = scale_inv
     assert t(P(A), 3, 16, E4, P(A + 4096), P(A + 8192), P(A + 9000), None) == fq.EDTYPE
     assert t(P(A), BF16, -5, E4, P(A + 4096), P(A + 8192), P(A + 9000), None) == fq.EINVAL
+    t = L.fp8q_cast_per_tensor_noalloc
+    assert t(P(A), BF16, -5, E4, P(A + 4096), P(A + 8192), None) == fq.EINVAL
+    assert t(P(A), 3, 16, E4, P(A + 4096), P(A + 8192), None) == fq.EDTYPE
+    assert t(P(A), BF16, 16, 7, P(A + 4096), P(A + 8192), None) == fq.EDTYPE
+    assert t(P(A), BF16, 16, E4, None, P(A + 8192), None) == fq.EINVAL
+    assert t(P(A), BF16, 16, E4, P(A + 4096), None, None) == fq.EINVAL
+    assert t(P(A + 1), BF16, 16, E4, P(A + 4096), P(A + 8192), None) == fq.EALIGN
+    assert t(P(A), BF16, 16, E4, P(A + 4096), P(A + 8194), None) == fq.EALIGN
+    assert t(P(A), BF16, 16, E4, P(A + 8), P(A + 8192), None) == fq.EINVAL                 # x/q overlap
+    assert t(P(A), BF16, 16, E4, P(A + 4096), P(A + 4100), None) == fq.EINVAL              # q/scale overlap
     c = L.fp8q_cast_per_channel
     assert c(P(A), F32, 4, 16, E5, P(A + 4096), None, None) == fq.EINVAL
     assert c(P(A + 2), F32, 4, 16, E5, P(A + 4096), P(A + 8192), None) == fq.EALIGN
@@ -216,7 +226,7 @@ def test_valid_calls_reach_the_launchers():
         assert fn(*args) == fq.OK, fn.__name__
         names = ("fill_f32", "amax", "amax_partials", "guard_amax", "cast_given_amax", "dequant_packed",
                  "pipeline_cast", "dequant_pipeline", "tensor_cast", "channel_cast", "group128_cast",
-                 "dequant_flat", "dequant_rows", "block128", "dequant_sum")
+                 "dequant_flat", "dequant_rows", "block128", "dequant_sum", "scratch_words")
         return {k: L.fp8q_stub_count(k.encode()) for k in names if L.fp8q_stub_count(k.encode())}
 
     x, q, s, y, ws, w = P(A), P(A + (1 << 20)), P(A + (2 << 20)), P(A + (3 << 20)), P(A + (4 << 20)), P(A + (5 << 20))
@@ -224,6 +234,9 @@ def test_valid_calls_reach_the_launchers():
     assert calls(L.fp8q_cast_per_group128, None, BF16, 0, 256, E4, None, None, None) == {}
     assert calls(L.fp8q_cast_per_tensor, x, F32, 16, E5, q, s, ws, None) == {"amax_partials": 1, "tensor_cast": 1}
     assert calls(L.fp8q_cast_per_tensor, None, F32, 0, E5, None, s, ws, None) == {"fill_f32": 1}
+    assert calls(L.fp8q_cast_per_tensor_noalloc, x, BF16, 16, E4, q, s, None) == \
+        {"scratch_words": 1, "amax_partials": 1, "tensor_cast": 1}
+    assert calls(L.fp8q_cast_per_tensor_noalloc, None, BF16, 0, E4, None, s, None) == {"fill_f32": 1}
     assert calls(L.fp8q_cast_per_channel, x, F16, 4, 16, E4, q, s, None) == {"channel_cast": 1}
     assert calls(L.fp8q_cast_per_channel, None, F16, 4, 0, E4, None, s, None) == {"fill_f32": 1}
     assert calls(L.fp8q_dequant_per_tensor, q, E4, 16, s, y, BF16, None) == {"dequant_flat": 1}
