@@ -97,6 +97,70 @@ def test_group_cast_edge_values():
         _check_cast(W.to_bf16_bits(x), "bf16", fmt)
 
 
+def _every_amax_groups(amax_bits: np.ndarray, dtype: str, seed: int) -> np.ndarray:
+    """One 128-group per amax value: the value itself, its negation, the
+    largest value below it, and 125 values of smaller magnitude with random
+    signs.  Every element's product with the group's scale is at most
+    amax * (fp8_max / amax) rounded, the largest product the non-saturating
+    kernels ever see."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    g = amax_bits.size
+    if dtype == "f32":
+        a = amax_bits.view(np.float32).astype(np.float64)
+    elif dtype == "bf16":
+        a = (amax_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    else:
+        a = amax_bits.view(np.float16).astype(np.float64)
+    mags = a[:, None] * rng.uniform(0.0, 1.0, size=(g, 125))
+    vals = mags * np.where(rng.integers(0, 2, size=(g, 125)) == 1, 1.0, -1.0)
+    f32 = vals.astype(np.float32)                       # |rounded| <= amax: rounding is monotone
+    if dtype == "f32":
+        body = f32.view(np.uint32)
+        below = np.maximum(amax_bits.astype(np.int64) - 1, 0).astype(np.uint32)
+        neg = amax_bits | np.uint32(0x80000000)
+        out = np.concatenate([amax_bits[:, None], neg[:, None], below[:, None], body], axis=1)
+        return out.view(np.float32)
+    body = W.to_bf16_bits(f32) if dtype == "bf16" else f32.astype(np.float16).view(np.uint16)
+    below = np.maximum(amax_bits.astype(np.int64) - 1, 0).astype(np.uint16)
+    neg = amax_bits | np.uint16(0x8000)
+    return np.concatenate([amax_bits[:, None], neg[:, None], below[:, None], body], axis=1)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("fmt", FMTS)
+def test_group_cast_every_amax(dtype, fmt):
+    """The non-saturating group kernels rely on amax * RN(fp8_max / amax)
+    encoding to the format's maximum code even when that product is one
+    binary32 ulp above fp8_max.  Every positive finite bf16 and fp16 value,
+    and 2^18 binary32 values spread over every exponent (half of them the
+    largest below a power of two times 448 or 57344), appears once as a
+    group's amax; each group must match the oracle bit-exactly."""
+    if dtype == "bf16":
+        amax = np.arange(1, 0x7F80, dtype=np.uint16)                 # 0x0001 .. 0x7F7F
+    elif dtype == "f16":
+        amax = np.arange(1, 0x7C00, dtype=np.uint16)                 # 0x0001 .. 0x7BFF
+    else:
+        rng = np.random.Generator(np.random.PCG64(41))
+        spread = rng.integers(1, 0x7F800000, size=1 << 17, dtype=np.uint32)
+        fmax = 448.0 if fmt == "e4m3fn" else 57344.0
+        k = rng.integers(-120, 100, size=1 << 17)
+        near = (np.ldexp(np.float64(fmax), k).astype(np.float32).view(np.uint32) -
+                rng.integers(0, 3, size=1 << 17).astype(np.uint32))
+        amax = np.concatenate([spread, near]).astype(np.uint32)
+    x = _every_amax_groups(amax, dtype, seed=42)
+    wq, _ = _check_cast(x, dtype, fmt)
+    code_max = 0x7E if fmt == "e4m3fn" else 0x7B
+    clamp = np.float32(1e-4)
+    if dtype == "f32":
+        a = amax.view(np.float32)
+    elif dtype == "bf16":
+        a = (amax.astype(np.uint32) << 16).view(np.float32)
+    else:
+        a = amax.view(np.float16).astype(np.float32)
+    big = a >= clamp                                  # unclamped groups: the amax element maps to +-max
+    assert np.all(wq[big, 0] == code_max) and np.all(wq[big, 1] == (code_max | 0x80))
+
+
 @pytest.mark.parametrize("ydtype", ["bf16", "f32", "f16"])
 @pytest.mark.parametrize("fmt", FMTS)
 def test_group_dequant(fmt, ydtype):
