@@ -362,6 +362,66 @@ k_group128(const void* __restrict__ x, uint8_t* __restrict__ q, float* __restric
     }
 }
 
+// Pair path, for x aligned to two elements but not to 16 bytes (a view that
+// starts a few elements into a buffer) and q aligned to 2 bytes: one
+// wavefront per 128-group, 64 lanes x 2 consecutive elements (one 4-byte
+// load for bf16 / fp16, one 8-byte load for fp32), the group max by a
+// 64-lane DPP reduction with no LDS round trip, and one 2-byte store of the
+// pair's codes per lane.  A wave takes G consecutive groups per trip, all
+// loaded before the first is converted.  This is the one-wavefront-per-group
+// shape; on the activation workload it takes about 100 us against 56 us for
+// k_group128's 16 lanes x 8 elements with 16-byte loads, so it only serves
+// inputs the 16-byte path cannot take.
+template <int DT, int FMT, int G>
+__global__ void __launch_bounds__(256)
+k_group128_pair(const void* __restrict__ x, uint8_t* __restrict__ q, float* __restrict__ sinv_out, int64_t groups) {
+    constexpr int ESZ = ESize<DT>::value;
+    const int lane = threadIdx.x & 63;
+    const int64_t trips = (groups + G - 1) / G;
+    const int64_t waves = (int64_t)gridDim.x * (blockDim.x / 64);
+    for (int64_t c = (int64_t)blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64; c < trips; c += waves) {
+        uint32_t w[G][ESZ / 2];     // the lane's two elements: one dword (16-bit types) or two (fp32)
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const int64_t g = c * G + j;
+            if (g < groups) {
+                const char* p = (const char*)x + (g * 128 + 2 * lane) * ESZ;
+                if constexpr (DT == kF32) {
+                    const v2u t = ld8<true>(p);
+                    w[j][0] = t.x;
+                    w[j][1] = t.y;
+                } else {
+                    w[j][0] = ld4<true>(p);
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const int64_t g = c * G + j;
+            if (g < groups) {   // uniform across the wave
+                uint32_t a;
+                float v0, v1;
+                if constexpr (DT == kF32) {
+                    a = umax(w[j][0] & 0x7FFFFFFFu, w[j][1] & 0x7FFFFFFFu);
+                    v0 = __uint_as_float(w[j][0]);
+                    v1 = __uint_as_float(w[j][1]);
+                } else {
+                    const uint32_t b = w[j][0] & 0x7FFF7FFFu;
+                    a = abs16_to_f32bits<DT>(umax(b & 0xFFFFu, b >> 16));
+                    if constexpr (DT == kBF16) { v0 = bf16_lo(w[j][0]); v1 = bf16_hi(w[j][0]); }
+                    else { v0 = f16_lo(w[j][0]); v1 = f16_hi(w[j][0]); }
+                }
+                const uint32_t m = max_lanes<64>(a);
+                float scale, sinv;
+                group_scale<FMT>(m, scale, sinv);
+                const uint32_t e = enc4<FMT>(v0 * scale, v1 * scale, 0.0f, 0.0f);
+                __builtin_nontemporal_store((uint16_t)(e & 0xFFFFu), (uint16_t*)(q + g * 128 + 2 * lane));
+                if (lane == 0) sinv_out[g] = sinv;
+            }
+        }
+    }
+}
+
 // Unaligned path: one wavefront per group, two elements per lane,
 // element-wise loads and byte stores; correct for any alignment of x (to its
 // element size) and q.
@@ -650,6 +710,22 @@ template <int FMT> __device__ __forceinline__ void channel_scale(uint32_t amax_b
     sinv = a / Fp8Fmt<FMT>::max;
 }
 
+// max over a 256-thread workgroup of R values at once, results valid in
+// every thread: DPP within each wave, then one LDS exchange and one barrier
+// pair for all R; every thread of the workgroup must call it
+template <int R> __device__ __forceinline__ void block_max256_rows(uint32_t* v, uint32_t* lds) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) v[r] = max_lanes<64>(v[r]);
+    if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) lds[r * 4 + (threadIdx.x >> 6)] = v[r];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < R; ++r) v[r] = umax(umax(lds[r * 4], lds[r * 4 + 1]), umax(lds[r * 4 + 2], lds[r * 4 + 3]));
+    __syncthreads();  // lds may be reused by the next trip
+}
+
 // Register-resident rows: cols % VE == 0, x 16-B aligned, q 4-byte aligned and
 // cols <= CPT * 256 * VE, so each thread keeps CPT lane vectors of the row in
 // VGPRs between the reduction and the cast (one HBM read per element).
@@ -686,6 +762,61 @@ k_channel_reg(const void* __restrict__ x, int64_t rows, int64_t cols, uint8_t* _
                 v[k].widen(f);
                 if (saturate) scale_encode_store<FMT, true, VE, NT>(f, scale, q + r * cols + vi * VE);
                 else scale_encode_store<FMT, false, VE, NT>(f, scale, q + r * cols + vi * VE);
+            }
+        }
+    }
+}
+
+// k_channel_reg for RPB consecutive rows per workgroup trip: all their loads
+// are issued before the one reduction barrier, so short rows keep more bytes
+// in flight per workgroup (bf16 [4096, 4096]: 10.7 us with two rows per trip
+// against 11.5 us with one).  The same preconditions per row.
+template <int DT, int FMT, int CPT, int RPB, bool NT>
+__global__ void __launch_bounds__(256)
+k_channel_rows(const void* __restrict__ x, int64_t rows, int64_t cols, uint8_t* __restrict__ q,
+              float* __restrict__ sinv_out) {
+    __shared__ uint32_t lds[4 * RPB];
+    constexpr int VE = LaneVE<DT>::value;
+    constexpr int ESZ = ESize<DT>::value;
+    const int64_t nvec = cols / VE;
+    for (int64_t r0 = (int64_t)blockIdx.x * RPB; r0 < rows; r0 += (int64_t)gridDim.x * RPB) {
+        HpVec<DT> v[RPB][CPT];
+        uint32_t m[RPB];
+#pragma unroll
+        for (int r = 0; r < RPB; ++r) {
+            const char* xr = (const char*)x + (r0 + r) * cols * ESZ;
+#pragma unroll
+            for (int k = 0; k < CPT; ++k) {
+                const int64_t vi = k * 256 + threadIdx.x;
+                if (r0 + r < rows && vi < nvec) v[r][k].template load<NT>(xr + vi * VE * ESZ);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < RPB; ++r) {
+            m[r] = 0;
+#pragma unroll
+            for (int k = 0; k < CPT; ++k)
+                if (r0 + r < rows && k * 256 + threadIdx.x < nvec) m[r] = umax(m[r], v[r][k].absmax_bits());
+        }
+        block_max256_rows<RPB>(m, lds);
+#pragma unroll
+        for (int r = 0; r < RPB; ++r) {
+            if (r0 + r < rows) {  // uniform across the workgroup
+                float scale, sinv;
+                channel_scale<FMT>(m[r], scale, sinv);
+                if (threadIdx.x == 0) sinv_out[r0 + r] = sinv;
+                const bool saturate = needs_saturation(m[r], scale);
+                uint8_t* qr = q + (r0 + r) * cols;
+#pragma unroll
+                for (int k = 0; k < CPT; ++k) {
+                    const int64_t vi = k * 256 + threadIdx.x;
+                    if (vi < nvec) {
+                        float f[VE];
+                        v[r][k].widen(f);
+                        if (saturate) scale_encode_store<FMT, true, VE, NT>(f, scale, qr + vi * VE);
+                        else scale_encode_store<FMT, false, VE, NT>(f, scale, qr + vi * VE);
+                    }
+                }
             }
         }
     }
@@ -899,6 +1030,49 @@ k_dequant_rows(const uint8_t* __restrict__ q, int64_t rows, int64_t cols, const 
     }
 }
 
+// Division of a 32-bit n by an invariant d >= 1 (Granlund-Montgomery):
+// with l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1 (computed on
+// the host), n / d = (umulhi(n, m) + n) >> l, exact for every 32-bit n.
+struct DivU32 {
+    uint32_t m;
+    int l;
+};
+__device__ __forceinline__ uint32_t div_u32(uint32_t n, DivU32 d) {
+    const uint32_t t = __umulhi(n, d.m);
+    return (uint32_t)(((uint64_t)t + n) >> d.l);
+}
+
+// per-channel, streamed flat: the [rows, cols] tensor is walked front to back
+// in chunks of K sub-steps x 256 lane vectors like the per-tensor dequant,
+// and each lane finds its row (and scale_inv[row], a cached load) by an
+// invariant-divisor division of its lane-vector index by the lane vectors
+// per row.  Short rows then need no workgroup per row.  Requires
+// cols % VE == 0, q 4-byte aligned, y 16-B aligned and rows * cols / VE < 2^32.
+template <int FMT, int YDT, int K, bool NT>
+__global__ void __launch_bounds__(256)
+k_dequant_rows_flat(const uint8_t* __restrict__ q, int64_t nvec, const float* __restrict__ sinv,
+                    void* __restrict__ y, DivU32 dvpr) {
+    constexpr int VE = LaneVE<YDT>::value;
+    const int64_t nchunks = (nvec + K * 256 - 1) / (K * 256);
+    for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+        Fp8Vec<FMT, VE, NT> w[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int64_t vi = (c * K + k) * 256 + threadIdx.x;
+            if (vi < nvec) w[k].load(q + vi * VE);
+        }
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int64_t vi = (c * K + k) * 256 + threadIdx.x;
+            if (vi < nvec) {
+                float p[VE];
+                w[k].decode_scaled(sinv[div_u32((uint32_t)vi, dvpr)], p);
+                store_out16<YDT, NT>(y, vi * VE, p);
+            }
+        }
+    }
+}
+
 // ===========================================================================
 // 128x128 block weight dequant (CSDN notes, weight_dequant_kernel)
 // ===========================================================================
@@ -946,18 +1120,6 @@ k_block128_rows(const uint8_t* __restrict__ q, int64_t M, int64_t N, const float
             }
         }
     }
-}
-
-// Division of a 32-bit n by an invariant d >= 1 (Granlund-Montgomery):
-// with l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1 (computed on
-// the host), n / d = (umulhi(n, m) + n) >> l, exact for every 32-bit n.
-struct DivU32 {
-    uint32_t m;
-    int l;
-};
-__device__ __forceinline__ uint32_t div_u32(uint32_t n, DivU32 d) {
-    const uint32_t t = __umulhi(n, d.m);
-    return (uint32_t)(((uint64_t)t + n) >> d.l);
 }
 
 // Flat mapping: the matrix is streamed front to back in chunks of K

@@ -17,6 +17,7 @@
 #include <algorithm>
 #include <atomic>
 #include <mutex>
+#include <type_traits>
 
 #include "fp8q_device.h"
 
@@ -45,6 +46,39 @@ inline unsigned grid(int64_t units) {
     return (unsigned)b;
 }
 
+// invariant-divisor constants for dividing a 32-bit lane-vector index by d >= 1
+inline DivU32 make_div(uint32_t d) {
+    int l = 0;
+    while ((uint64_t(1) << l) < d) ++l;
+    return DivU32{(uint32_t)((((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d) + 1), l};
+}
+
+template <int K> using KC = std::integral_constant<int, K>;
+
+// Sub-steps per chunk (K) of a flat kernel over u1 = ceil(nvec / 256) chunks
+// of one sub-step, with a grid covering the tensor.  K = 2 in general; a
+// tensor whose K = 2 grid would take two to four dispatch rounds of
+// workgroups (256 CUs x 8 resident workgroups = 2048 per round) instead gets
+// the K that brings the grid to about one round.  Measured on the flat
+// dequants, e4m3fn -> bf16 / fp32 from 2^20 to 2^27 elements: bf16 2^24
+// 10.0 us with K = 4 against 11.4 us with K = 2; fp32 2^23 8.3-8.5 against
+// 9.9 us; at 2^25 elements and above K = 2 is fastest again (bf16 2^27: 66.6
+// us against 71.1 with K = 4), and below 2^23 the choice makes no difference.
+inline int pick_flat_k(int64_t u1) {
+    if (u1 > 4096 && u1 <= 8192) return 4;
+    if (u1 > 8192 && u1 <= 16384) return 8;
+    return 2;
+}
+
+// launch(KC<K>{}, grid) for the K pick_flat_k chooses over nvec lane vectors
+template <typename L> void launch_k(int64_t nvec, L&& launch) {
+    const int64_t u1 = (nvec + 255) / 256;
+    const int K = pick_flat_k(u1);
+    if (K == 8) launch(KC<8>{}, grid((u1 + 7) / 8));
+    else if (K == 4) launch(KC<4>{}, grid((u1 + 3) / 4));
+    else launch(KC<2>{}, grid((u1 + 1) / 2));
+}
+
 template <template <int, int> class F, typename... A>
 void dispatch_dt_fmt(int dt, int fmt, A... a) {
     if (dt == kF32) { if (fmt == kE4M3) F<kF32, kE4M3>::run(a...); else F<kF32, kE5M2>::run(a...); }
@@ -63,12 +97,18 @@ void dispatch_fmt_ydt(int fmt, int ydt, A... a) {
     }
 }
 
+constexpr int kPairG = 8;          // groups per wave trip in the pair path
+
 template <int DT, int FMT> struct RunGroup128 {
     static void run(const void* x, int64_t groups, uint8_t* q, float* sinv, hipStream_t st) {
         constexpr int VE = LaneVE<DT>::value;
+        constexpr int ESZ = ESize<DT>::value;
         if (al(x, 16) && al(q, 4)) {
             constexpr int64_t CH = kGroupK * (256 / (128 / VE));
             k_group128<DT, FMT, kGroupK, kNT><<<grid((groups + CH - 1) / CH), kThreads, 0, st>>>(x, q, sinv, groups);
+        } else if (al(x, 2 * ESZ) && al(q, 2)) {
+            const int64_t trips = (groups + kPairG - 1) / kPairG;
+            k_group128_pair<DT, FMT, kPairG><<<grid((trips + 3) / 4), kThreads, 0, st>>>(x, q, sinv, groups);
         } else {
             k_group128_wave<DT, FMT><<<grid((groups + 3) / 4), kThreads, 0, st>>>(x, q, sinv, groups);
         }
@@ -78,6 +118,10 @@ template <int DT, int FMT> struct RunGroup128 {
 // cached: ordinary loads and stores instead of non-temporal ones, for a
 // cast pass whose input was just written by the previous kernel (the
 // reduce step's re-cast: 90.4 us against 93.1 us for 8 x 2^25 e5m2 chunks)
+// The cast pass keeps K = kAmaxK = 2 at every size, so that chunk c is cast
+// by workgroup c on the XCD whose L2 the amax pass loaded it into (amax
+// workgroup c mod 1024); the fatter chunks pick_flat_k gives the dequants
+// would break that pairing (bf16 [4096, 4096]: 16.5 us against 15.1 us).
 template <int DT, int FMT> struct RunTensorCast {
     static void run(const void* x, int64_t n, const uint32_t* partial, int np, int pstride, uint8_t* q, float* sinv,
                     bool cached, hipStream_t st) {
@@ -106,12 +150,27 @@ template <int DT, int FMT> struct RunCastGivenAmax {
     }
 };
 
+// Per-channel cast.  16-bit rows of up to 512 lane vectors (4096 elements)
+// take two rows per workgroup trip (their loads in flight together); wider
+// rows and fp32 take one row per workgroup (fp32 [4096, 4096]: 17.0 us with
+// one row, 17.2-17.9 us with two).
 template <int DT, int FMT> struct RunChannel {
     static void run(const void* x, int64_t rows, int64_t cols, uint8_t* q, float* sinv, hipStream_t st) {
         constexpr int VE = LaneVE<DT>::value;
         const bool vec = (cols % VE == 0) && al(x, 16) && al(q, 4);
         const int64_t nvec = cols / VE;
         const unsigned nb = grid(rows);
+        if constexpr (DT != kF32) {
+            const unsigned nb2 = grid((rows + 1) / 2);
+            if (vec && nvec <= 256) {
+                k_channel_rows<DT, FMT, 1, 2, kNT><<<nb2, kThreads, 0, st>>>(x, rows, cols, q, sinv);
+                return;
+            }
+            if (vec && nvec <= 512) {
+                k_channel_rows<DT, FMT, 2, 2, kNT><<<nb2, kThreads, 0, st>>>(x, rows, cols, q, sinv);
+                return;
+            }
+        }
         if (vec && nvec <= 256) k_channel_reg<DT, FMT, 1, kNT><<<nb, kThreads, 0, st>>>(x, rows, cols, q, sinv);
         else if (vec && nvec <= 512) k_channel_reg<DT, FMT, 2, kNT><<<nb, kThreads, 0, st>>>(x, rows, cols, q, sinv);
         else if (vec && nvec <= 1024) k_channel_reg<DT, FMT, 4, kNT><<<nb, kThreads, 0, st>>>(x, rows, cols, q, sinv);
@@ -166,20 +225,21 @@ template <int DT> int run_amax_partials(const void* x, int64_t n, uint32_t* part
 }
 
 template <int FMT, int YDT> struct RunDequantFlat {
-    static void run(int mode, const uint8_t* q, int64_t n, const float* sinv, void* y, hipStream_t st) {
+    template <int MODE> static void go(const uint8_t* q, int64_t n, const float* sinv, void* y, hipStream_t st) {
         constexpr int VE = LaneVE<YDT>::value;
-        const bool vec = al(q, 4) && al(y, 16);
-        const unsigned nb = vec ? grid((n / VE + kFlatK * 256 - 1) / (kFlatK * 256)) : grid((n + 255) / 256);
-        if (mode == 0) {
-            if (vec) k_dequant_flat<FMT, YDT, 0, true, kFlatK, kNT><<<nb, kThreads, 0, st>>>(q, n, sinv, y);
-            else k_dequant_flat<FMT, YDT, 0, false, kFlatK, kNT><<<nb, kThreads, 0, st>>>(q, n, sinv, y);
-        } else if (mode == 3) {
-            if (vec) k_dequant_flat<FMT, YDT, 3, true, kFlatK, kNT><<<nb, kThreads, 0, st>>>(q, n, sinv, y);
-            else k_dequant_flat<FMT, YDT, 3, false, kFlatK, kNT><<<nb, kThreads, 0, st>>>(q, n, sinv, y);
+        if (al(q, 4) && al(y, 16)) {
+            launch_k(n / VE, [&](auto K, unsigned nb) {
+                k_dequant_flat<FMT, YDT, MODE, true, decltype(K)::value, kNT><<<nb, kThreads, 0, st>>>(q, n, sinv, y);
+            });
         } else {
-            if (vec) k_dequant_flat<FMT, YDT, 2, true, kFlatK, kNT><<<nb, kThreads, 0, st>>>(q, n, sinv, y);
-            else k_dequant_flat<FMT, YDT, 2, false, kFlatK, kNT><<<nb, kThreads, 0, st>>>(q, n, sinv, y);
+            k_dequant_flat<FMT, YDT, MODE, false, kFlatK, kNT><<<grid((n + 255) / 256), kThreads, 0, st>>>(q, n, sinv,
+                                                                                                           y);
         }
+    }
+    static void run(int mode, const uint8_t* q, int64_t n, const float* sinv, void* y, hipStream_t st) {
+        if (mode == 0) go<0>(q, n, sinv, y, st);
+        else if (mode == 3) go<3>(q, n, sinv, y, st);
+        else go<2>(q, n, sinv, y, st);
     }
 };
 
@@ -225,8 +285,17 @@ template <int FMT, int YDT> struct RunDequantRows {
     static void run(const uint8_t* q, int64_t rows, int64_t cols, const float* sinv, void* y, hipStream_t st) {
         constexpr int VE = LaneVE<YDT>::value;
         const bool vec = (cols % VE == 0) && al(q, 4) && al(y, 16);
-        if (vec) k_dequant_rows<FMT, YDT, true, kNT><<<grid(rows), kThreads, 0, st>>>(q, rows, cols, sinv, y);
-        else k_dequant_rows<FMT, YDT, false, kNT><<<grid(rows), kThreads, 0, st>>>(q, rows, cols, sinv, y);
+        const int64_t nvec = rows * (cols / VE);
+        if (vec && nvec < (int64_t(1) << 32)) {
+            const DivU32 dv = make_div((uint32_t)(cols / VE));
+            launch_k(nvec, [&](auto K, unsigned nb) {
+                k_dequant_rows_flat<FMT, YDT, decltype(K)::value, kNT><<<nb, kThreads, 0, st>>>(q, nvec, sinv, y, dv);
+            });
+        } else if (vec) {
+            k_dequant_rows<FMT, YDT, true, kNT><<<grid(rows), kThreads, 0, st>>>(q, rows, cols, sinv, y);
+        } else {
+            k_dequant_rows<FMT, YDT, false, kNT><<<grid(rows), kThreads, 0, st>>>(q, rows, cols, sinv, y);
+        }
     }
 };
 
@@ -236,11 +305,8 @@ template <int FMT, int YDT> struct RunBlock128 {
         const int64_t nbn = (N + 127) / 128;
         const int64_t nvec = M * (N / VE);
         if (N % VE == 0 && al(q, 4) && al(y, 16) && nvec < (int64_t(1) << 32)) {
-            // invariant-divisor magic for dividing a lane-vector index by N / VE
             const uint32_t vpr = (uint32_t)(N / VE);
-            int l = 0;
-            while ((uint64_t(1) << l) < vpr) ++l;
-            const DivU32 dv{(uint32_t)((((uint64_t(1) << 32) * ((uint64_t(1) << l) - vpr)) / vpr) + 1), l};
+            const DivU32 dv = make_div(vpr);
             const int64_t chunks = (nvec + kBlockK * 256 - 1) / (kBlockK * 256);
             k_block128_flat<FMT, YDT, kBlockK, kNT><<<grid(chunks), kThreads, 0, st>>>(q, nvec, sinv, y, nbn, vpr, dv);
         } else if (N % VE == 0 && al(q, 4) && al(y, 16)) {

@@ -68,10 +68,15 @@ def test_group_cast_shapes(dtype, fmt, rows, cols):
     _check_cast(_inputs(dtype, rows, cols, seed=rows * 7 + cols), dtype, fmt)
 
 
-@pytest.mark.parametrize("x_offset,q_offset", [(1, 0), (0, 3), (3, 5)])
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+# x offset by 1 or 3 elements, or q by an odd count: the element-wise kernel;
+# x offset by an even count but not 16-byte aligned, q even: the pair kernel
+# (one wavefront per group, two elements per lane)
+@pytest.mark.parametrize("x_offset,q_offset", [(1, 0), (0, 3), (3, 5), (2, 0), (2, 2), (4, 6), (2, 1)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "f16"])
 def test_group_cast_unaligned(dtype, x_offset, q_offset):
-    _check_cast(_inputs(dtype, 33, 384, seed=5), dtype, "e4m3fn", x_offset=x_offset, q_offset=q_offset)
+    for fmt in FMTS:
+        _check_cast(_inputs(dtype, 33, 384, seed=5), dtype, fmt, x_offset=x_offset, q_offset=q_offset)
+        _check_cast(_inputs(dtype, 70, 1152, seed=6), dtype, fmt, x_offset=x_offset, q_offset=q_offset)
 
 
 def test_group_cast_edge_values():

@@ -115,6 +115,41 @@ def test_tensor_sizes(n, dtype):
     _check_tensor(x, dtype, "e4m3fn", x_offset=1)           # unaligned x -> element-wise kernel
 
 
+@pytest.mark.parametrize("dtype,n", [("bf16", 9_000_003), ("f32", 13_000_001), ("bf16", 30_000_007),
+                                     ("f16", 20_000_001)])
+def test_tensor_sizes_fat_chunks(dtype, n):
+    """Sizes whose flat kernels take K = 4 or 8 sub-steps per chunk (the
+    launch picks them when the K = 2 grid would span two to four dispatch
+    rounds), with ragged tails: cast, then dequant to bf16 and fp32."""
+    rng = np.random.Generator(np.random.PCG64(n))
+    x = rng.standard_normal(n, dtype=np.float32) * np.float32(5.0)
+    if dtype == "bf16":
+        x = W.to_bf16_bits(x)
+    elif dtype == "f16":
+        x = x.astype(np.float16).view(np.uint16)
+    for fmt in FMTS:
+        q, s = _check_tensor(x, dtype, fmt)
+        for ydt in ("bf16", "f32"):
+            assert_hp_equal(_dequant(q, s, fmt, ydt, False), oracle.dequant_per_tensor(q, fmt, s, ydt), ydt,
+                            f"per-tensor dequant n={n} {fmt}->{ydt}")
+
+
+@pytest.mark.parametrize("rows,cols", [(3001, 4000), (2049, 7000), (1, 8_400_000), (4097, 2048), (7, 4096)])
+def test_channel_fat_chunks_and_row_pairs(rows, cols):
+    """Per-channel cast with two rows per workgroup trip (16-bit rows of up to
+    4096 elements, odd row counts leave a half trip) and the flat per-channel
+    dequant at sizes where it takes K = 4 or 8, with row lengths that are not
+    powers of two (the lane's row comes from an invariant-divisor division)."""
+    xf = _rows_scaled(rows, cols, seed=rows * 3 + cols)["f32"]
+    for dtype in ("bf16", "f16", "f32"):
+        x = {"f32": xf, "bf16": W.to_bf16_bits(xf),
+             "f16": np.clip(xf, -6e4, 6e4).astype(np.float16).view(np.uint16)}[dtype]
+        q, s = _check_channel(x, dtype, "e4m3fn")
+    for ydt in ("bf16", "f32"):
+        assert_hp_equal(_dequant(q, s, "e4m3fn", ydt, True), oracle.dequant_per_channel(q, "e4m3fn", s, ydt), ydt,
+                        f"per-channel dequant [{rows}, {cols}] -> {ydt}")
+
+
 def test_amax_entry_point():
     for dtype, n in [("bf16", 1 << 20), ("f32", 12345), ("f16", 77)]:
         rng = np.random.Generator(np.random.PCG64(n))
