@@ -413,6 +413,31 @@ def _other_rows(fq, W, np, torch, dev, st, iters, log, HE, act, roundtrip):
         into[name] = _row(nbytes, us, elems)
         log(f"{name}: {into[name]['avg_us']} us, {into[name]['gbps']} GB/s")
 
+    # the per-128-group dequant of the step on its own, after a flush: the step
+    # runs it right after the cast wrote q, so this row shows what the step's
+    # dequant would take with q coming from HBM instead of the Infinity Cache
+    Ra, Ca = act.shape
+    qa8 = torch.empty((Ra, Ca), dtype=torch.uint8, device=dev)
+    sa8 = torch.empty((Ra, Ca // 128), dtype=torch.float32, device=dev)
+    ya8 = torch.empty((Ra, Ca), dtype=torch.bfloat16, device=dev)
+    with torch.cuda.stream(st):
+        fq.fp8q_cast_per_group128(act, qa8, sa8, "e4m3fn", stream=st)
+    timed("group128_dequant_e4m3fn_bf16_16384x7168 (flushed, q from HBM)", Ra * Ca + Ra * (Ca // 128) * 4 + Ra * Ca * 2,
+          Ra * Ca, lambda: fq.fp8q_dequant_per_group128(qa8, sa8, ya8, "e4m3fn", stream=st))
+    del ya8
+    # the same cast from views that start two elements into their buffers
+    # (4-byte aligned, not 16): the pair kernel, one wavefront per 128-group
+    # with two bf16 per lane -- the shape the per-group cast is often described
+    # with, next to the 16-lane / 16-byte k_group128 of the headline row
+    xo = torch.empty(Ra * Ca + 2, dtype=torch.bfloat16, device=dev)
+    xo[2:].copy_(act.reshape(-1))
+    qo = torch.empty(Ra * Ca + 2, dtype=torch.uint8, device=dev)
+    xv, qv = xo[2:].view(Ra, Ca), qo[2:].view(Ra, Ca)
+    timed("group128_cast_bf16_e4m3fn_16384x7168 (x, q two elements into their buffers: k_group128_pair, "
+          "one wavefront per group, 4-byte loads)", Ra * Ca * 3 + Ra * (Ca // 128) * 4, Ra * Ca,
+          lambda: fq.fp8q_cast_per_group128(xv, qv, sa8, "e4m3fn", stream=st))
+    del xo, qo, xv, qv, qa8, sa8
+
     # pipeline p2p cast of the activation (bf16 [16384, 7168]) with the format
     # chosen on the device, and back to bf16
     na = act.numel()
@@ -520,14 +545,15 @@ def _other_rows(fq, W, np, torch, dev, st, iters, log, HE, act, roundtrip):
         s1 = torch.empty(1, dtype=torch.float32, device=dev)
         sr = torch.empty(R, dtype=torch.float32, device=dev)
         y = torch.empty((R, C), dtype=xd.dtype, device=dev)
-        timed(f"per_tensor_cast_{dt}_e4m3fn_4096x4096 (2 passes)", 2 * R * C * esz + R * C + 4, R * C,
-              lambda: fq.fp8q_cast_per_tensor(xd, q, s1, ws, "e4m3fn", stream=st))
-        timed(f"per_tensor_dequant_e4m3fn_{dt}_4096x4096", R * C + 4 + R * C * esz, R * C,
-              lambda: fq.fp8q_dequant_per_tensor(q, s1, y, "e4m3fn", stream=st))
-        timed(f"per_channel_cast_{dt}_e4m3fn_4096x4096", R * C * esz + R * C + R * 4, R * C,
-              lambda: fq.fp8q_cast_per_channel(xd, q, sr, "e4m3fn", stream=st))
-        timed(f"per_channel_dequant_e4m3fn_{dt}_4096x4096", R * C + R * 4 + R * C * esz, R * C,
-              lambda: fq.fp8q_dequant_per_channel(q, sr, y, "e4m3fn", stream=st))
+        for fmt in ("e4m3fn", "e5m2"):        # the configuration covers both formats
+            timed(f"per_tensor_cast_{dt}_{fmt}_4096x4096 (2 passes)", 2 * R * C * esz + R * C + 4, R * C,
+                  lambda: fq.fp8q_cast_per_tensor(xd, q, s1, ws, fmt, stream=st))
+            timed(f"per_tensor_dequant_{fmt}_{dt}_4096x4096", R * C + 4 + R * C * esz, R * C,
+                  lambda: fq.fp8q_dequant_per_tensor(q, s1, y, fmt, stream=st))
+            timed(f"per_channel_cast_{dt}_{fmt}_4096x4096", R * C * esz + R * C + R * 4, R * C,
+                  lambda: fq.fp8q_cast_per_channel(xd, q, sr, fmt, stream=st))
+            timed(f"per_channel_dequant_{fmt}_{dt}_4096x4096", R * C + R * 4 + R * C * esz, R * C,
+                  lambda: fq.fp8q_dequant_per_channel(q, sr, y, fmt, stream=st))
         del xd, q, y
     # context for the short rows above: torch's device copy of the same byte
     # volumes (half read, half written), timed the same way
