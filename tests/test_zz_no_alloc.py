@@ -73,3 +73,36 @@ def test_noalloc_empty_and_binding():
     wq, wsi = oracle.cast_per_tensor(xh, "bf16", "e5m2")
     assert_fp8_equal(host(q), wq, "e5m2", "binding q")
     assert_f32_equal(host(si), wsi, "binding scale_inv")
+
+
+def test_noalloc_under_graph_capture():
+    """The callers this entry point exists for include code under HIP graph
+    capture: capture it (no allocation inside the capture), replay the graph
+    four times with eager work that scribbles over the outputs in between, and
+    check every replay against an eager call."""
+    n = 3_000_005
+    xh = _input(n, "bf16", None, 76)
+    x = dev(xh, "bf16")
+    q, si = G.empty(n, dtype=torch.uint8), G.empty(1, dtype=torch.float32)
+    fq.fp8q_cast_per_tensor_noalloc(x, q, si, "e4m3fn")          # eager call (also warms the lookup)
+    torch.cuda.synchronize()
+    want_q, want_s = host(q).copy(), host(si).copy()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            fq.fp8q_cast_per_tensor_noalloc(x, q, si, "e4m3fn", stream=s)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        q.fill_(0xA5)
+        si.fill_(-1.0)
+        torch.cuda.synchronize()
+        print(f"[case] noalloc graph replay {rep}", flush=True)
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(q), want_q), rep
+        assert np.array_equal(host(si).view(np.uint32), want_s.view(np.uint32)), rep
+    wq, wsi = oracle.cast_per_tensor(xh, "bf16", "e4m3fn")
+    assert_fp8_equal(want_q, wq, "e4m3fn", "graph q vs oracle")
+    assert_f32_equal(want_s, wsi, "graph scale_inv vs oracle")
