@@ -9,6 +9,9 @@
 // one chunk of K = 2 sub-steps per workgroup with a grid covering the whole
 // tensor (measured faster than fewer, looping workgroups); non-temporal
 // loads and stores for the streaming data (1.5-1.8x faster than cached).
+// Flat dequants, and both passes of the two-pass casts, over 1-4 M lane
+// vectors (8-32 M 16-bit elements, 4-16 M fp32 elements) take K = 4 or 8
+// instead (pick_flat_k), which brings their grid to about one dispatch round.
 // The amax passes are the exception: their grid is capped at kAmaxGrid
 // workgroups that loop over chunks.  In the stand-alone amax every workgroup
 // ends in one atomic max on a single word, and those serialise across the 8
@@ -30,7 +33,7 @@ constexpr int64_t kAmaxGrid = kAmaxPartials;  // amax-pass workgroups (and parti
 constexpr int64_t kSumAmaxGrid = 8192;  // the reduce step's sum pass when it also folds the amax
 
 constexpr int kGroupK = 2;        // sub-steps per group-cast chunk
-constexpr int kFlatK = 2;         // sub-steps per flat cast / dequant chunk
+constexpr int kFlatK = 2;         // sub-steps per flat chunk outside pick_flat_k's window
 constexpr int kAmaxK = 2;         // sub-steps per amax chunk
 constexpr int kBlockK = 2;        // sub-steps per block-dequant chunk
 constexpr int kBlockRows = 1;     // rows per workgroup in the row-strip fallback
@@ -118,22 +121,31 @@ template <int DT, int FMT> struct RunGroup128 {
 // cached: ordinary loads and stores instead of non-temporal ones, for a
 // cast pass whose input was just written by the previous kernel (the
 // reduce step's re-cast: 90.4 us against 93.1 us for 8 x 2^25 e5m2 chunks)
-// The cast pass keeps K = kAmaxK = 2 at every size, so that chunk c is cast
-// by workgroup c on the XCD whose L2 the amax pass loaded it into (amax
-// workgroup c mod 1024); the fatter chunks pick_flat_k gives the dequants
-// would break that pairing (bf16 [4096, 4096]: 16.5 us against 15.1 us).
+// The cast pass takes the same sub-steps per chunk as the amax pass before it
+// (pick_flat_k over the tensor's lane vectors, in both), so that chunk c is
+// cast by workgroup c on the XCD whose L2 the amax pass loaded it into (amax
+// workgroup c mod 1024).  A fatter cast chunk over K = 2 amax chunks broke
+// that pairing (bf16 [4096, 4096]: 16.5 us against 15.1 us); fatter chunks in
+// both passes keep it and gain (14.7 against 15.3 us; fp32 26.3 against 27.2).
+// The reduce step's re-cast (cached) folds amax slots, not partials, and
+// keeps K = 2.
 template <int DT, int FMT> struct RunTensorCast {
     static void run(const void* x, int64_t n, const uint32_t* partial, int np, int pstride, uint8_t* q, float* sinv,
                     bool cached, hipStream_t st) {
         constexpr int VE = LaneVE<DT>::value;
         const bool vec = al(x, 16) && al(q, 4);
-        const unsigned nb = vec ? grid((n / VE + kFlatK * 256 - 1) / (kFlatK * 256)) : grid((n + 255) / 256);
-        if (vec && cached)
+        if (vec && cached) {
+            const unsigned nb = grid((n / VE + kFlatK * 256 - 1) / (kFlatK * 256));
             k_tensor_cast<DT, FMT, true, kFlatK, false><<<nb, kThreads, 0, st>>>(x, n, partial, np, pstride, q, sinv);
-        else if (vec)
-            k_tensor_cast<DT, FMT, true, kFlatK, kNT><<<nb, kThreads, 0, st>>>(x, n, partial, np, pstride, q, sinv);
-        else
-            k_tensor_cast<DT, FMT, false, kFlatK, kNT><<<nb, kThreads, 0, st>>>(x, n, partial, np, pstride, q, sinv);
+        } else if (vec) {
+            launch_k(n / VE, [&](auto K, unsigned nb) {
+                k_tensor_cast<DT, FMT, true, decltype(K)::value, kNT><<<nb, kThreads, 0, st>>>(x, n, partial, np,
+                                                                                               pstride, q, sinv);
+            });
+        } else {
+            k_tensor_cast<DT, FMT, false, kFlatK, kNT><<<grid((n + 255) / 256), kThreads, 0, st>>>(x, n, partial, np,
+                                                                                                  pstride, q, sinv);
+        }
     }
 };
 
@@ -211,16 +223,30 @@ template <int DT> void run_amax(const void* x, int64_t n, uint32_t* word, hipStr
 // bf16 [4096, 4096]: 20.5 us against 26.9 us with non-temporal loads).
 // Two launches instead of four (slot clear, atomics, slot fold): the bf16
 // [4096, 4096] cast takes 16.4 us against 20.8 us, fp32 28.5 against 31.9.
+// The vector amax pass takes the sub-steps per chunk its cast pass will take
+// (pick_flat_k, see RunTensorCast); the element-wise one takes kAmaxK.
 template <int DT> int amax_partials_grid(const void* x, int64_t n) {
     constexpr int VE = LaneVE<DT>::value;
-    const int64_t units = al(x, 16) ? (n / VE + kAmaxK * 256 - 1) / (kAmaxK * 256) : (n + 255) / 256;
+    int64_t units = (n + 255) / 256;
+    if (al(x, 16)) {
+        const int64_t u1 = (n / VE + 255) / 256;
+        const int K = pick_flat_k(u1);
+        units = (u1 + K - 1) / K;
+    }
     return (int)std::min(std::max<int64_t>(units, 1), kAmaxGrid);
 }
 
 template <int DT> int run_amax_partials(const void* x, int64_t n, uint32_t* partial, hipStream_t st) {
+    constexpr int VE = LaneVE<DT>::value;
     const int g = amax_partials_grid<DT>(x, n);
-    if (al(x, 16)) k_amax<DT, true, kAmaxK, false, true><<<g, kThreads, 0, st>>>(x, n, partial, 0);
-    else k_amax<DT, false, kAmaxK, false, true><<<g, kThreads, 0, st>>>(x, n, partial, 0);
+    if (al(x, 16)) {
+        const int K = pick_flat_k((n / VE + 255) / 256);
+        if (K == 8) k_amax<DT, true, 8, false, true><<<g, kThreads, 0, st>>>(x, n, partial, 0);
+        else if (K == 4) k_amax<DT, true, 4, false, true><<<g, kThreads, 0, st>>>(x, n, partial, 0);
+        else k_amax<DT, true, 2, false, true><<<g, kThreads, 0, st>>>(x, n, partial, 0);
+    } else {
+        k_amax<DT, false, kAmaxK, false, true><<<g, kThreads, 0, st>>>(x, n, partial, 0);
+    }
     return g;
 }
 
@@ -246,10 +272,11 @@ template <int FMT, int YDT> struct RunDequantFlat {
 template <int DT> void run_pipeline_cast(const void* x, int64_t n, const uint32_t* partial, int np, uint8_t* q,
                                          float* sinv, int32_t* fmt_out, hipStream_t st) {
     constexpr int VE = LaneVE<DT>::value;
-    if (al(x, 16) && al(q, 4)) {
-        const int64_t chunks = (n / VE + kFlatK * 256 - 1) / (kFlatK * 256);
-        k_pipeline_cast<DT, true, kFlatK, kNT><<<grid(chunks), kThreads, 0, st>>>(x, n, partial, np, q, sinv,
-                                                                                  fmt_out);
+    if (al(x, 16) && al(q, 4)) {   // the amax pass's sub-steps per chunk (RunTensorCast)
+        launch_k(n / VE, [&](auto K, unsigned nb) {
+            k_pipeline_cast<DT, true, decltype(K)::value, kNT><<<nb, kThreads, 0, st>>>(x, n, partial, np, q, sinv,
+                                                                                        fmt_out);
+        });
     } else {
         k_pipeline_cast<DT, false, kFlatK, kNT><<<grid((n + 255) / 256), kThreads, 0, st>>>(x, n, partial, np, q,
                                                                                              sinv, fmt_out);

@@ -65,6 +65,13 @@ def test_packed_shapes(fmt, dtype):
         _round_trip(_inputs(Wn, n, dtype, seed=Wn * 7 + n), dtype, fmt, ("bf16", "f32", "f16"), what="shape")
 
 
+def test_packed_fat_chunks():
+    """Slot casts whose amax and cast passes take 4 or 8 sub-steps per chunk."""
+    _round_trip(_inputs(2, 9_000_004, "bf16", seed=31), "bf16", "e5m2", ("bf16",), what="fat K=4")
+    _round_trip(_inputs(1, 30_000_000, "bf16", seed=32), "bf16", "e4m3fn", ("f32",), what="fat K=8")
+    _round_trip(_inputs(2, 12_000_000, "f32", seed=33), "f32", "e5m2", ("bf16",), what="fat f32 K=8")
+
+
 def test_packed_base_offsets():
     """The combined buffer at 4, 8 and 12 bytes past a 16-B boundary."""
     for off in (4, 8, 12):

@@ -65,6 +65,16 @@ def test_pipeline_sizes_and_formats(dtype):
     assert seen == {"e4m3fn", "e5m2"}
 
 
+@pytest.mark.parametrize("dtype,n", [("bf16", 9_000_007), ("f32", 12_000_001), ("f16", 30_000_003)])
+def test_pipeline_fat_chunks(dtype, n):
+    """Sizes whose amax and cast passes both take 4 or 8 sub-steps per chunk,
+    with ragged tails."""
+    rng = np.random.Generator(np.random.PCG64(n))
+    for e in (0.0, 3.0):
+        x = (rng.standard_normal(n) * 10.0 ** e).astype(np.float32)
+        _check_pipeline(_to_dtype(x, dtype), dtype, f"fat chunks N(0,1e{e:g})", ydtypes=("bf16",))
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32", "f16"])
 def test_pipeline_unaligned(dtype):
     rng = np.random.Generator(np.random.PCG64(62))
