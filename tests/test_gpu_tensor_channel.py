@@ -150,6 +150,54 @@ def test_channel_fat_chunks_and_row_pairs(rows, cols):
                         f"per-channel dequant [{rows}, {cols}] -> {ydt}")
 
 
+def _every_amax_values(dtype, fmt):
+    """The amax bit patterns of test_gpu_group128.test_group_cast_every_amax:
+    every positive finite bf16 / fp16 value, or 2^18 binary32 values over every
+    exponent (half of them just below a power of two times fp8_max)."""
+    if dtype == "bf16":
+        return np.arange(1, 0x7F80, dtype=np.uint16)
+    if dtype == "f16":
+        return np.arange(1, 0x7C00, dtype=np.uint16)
+    rng = np.random.Generator(np.random.PCG64(43))
+    spread = rng.integers(1, 0x7F800000, size=1 << 17, dtype=np.uint32)
+    k = rng.integers(-120, 100, size=1 << 17)
+    near = (np.ldexp(np.float64(FP8_MAX[fmt]), k).astype(np.float32).view(np.uint32) -
+            rng.integers(0, 3, size=1 << 17).astype(np.uint32))
+    return np.concatenate([spread, near]).astype(np.uint32)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("fmt", FMTS)
+def test_channel_and_tensor_cast_every_amax(dtype, fmt):
+    """The per-channel and per-tensor casts skip the clamp whenever amax > 0 and
+    the scale is finite, so they rely, like the group cast, on amax *
+    RN(fp8_max / amax) encoding to the maximum code when that product is one
+    binary32 ulp above fp8_max.  Per-channel: one row per amax value (the value,
+    its negation, the value below it, 125 smaller ones).  Per-tensor: 64 of
+    those rows, one call each, chosen where the product rounds above fp8_max."""
+    from test_gpu_group128 import _every_amax_groups
+    amax = _every_amax_values(dtype, fmt)
+    x = _every_amax_groups(amax, dtype, seed=44)
+    q, s = _check_channel(x, dtype, fmt)
+    code_max = 0x7E if fmt == "e4m3fn" else 0x7B
+    assert np.all(q[:, 0] == code_max) and np.all(q[:, 1] == (code_max | 0x80))
+    # rows whose product amax * fl32(fp8_max / amax) exceeds fp8_max in exact arithmetic
+    if dtype == "f32":
+        a = amax.view(np.float32)
+    elif dtype == "bf16":
+        a = (amax.astype(np.uint32) << 16).view(np.float32)
+    else:
+        a = amax.view(np.float16).astype(np.float32)
+    with np.errstate(over="ignore", divide="ignore"):
+        scale = (np.float32(FP8_MAX[fmt]) / a).astype(np.float32)
+    over = np.nonzero(np.isfinite(scale) & (a.astype(np.float64) * scale.astype(np.float64) > FP8_MAX[fmt]))[0]
+    assert over.size > 0
+    rng = np.random.Generator(np.random.PCG64(45))
+    for r in rng.choice(over, size=min(64, over.size), replace=False):
+        qt, _ = _check_tensor(x[r:r + 1], dtype, fmt)
+        assert qt.reshape(-1)[0] == code_max and qt.reshape(-1)[1] == (code_max | 0x80)
+
+
 def test_amax_entry_point():
     for dtype, n in [("bf16", 1 << 20), ("f32", 12345), ("f16", 77)]:
         rng = np.random.Generator(np.random.PCG64(n))
