@@ -9,9 +9,11 @@
 // one chunk of K = 2 sub-steps per workgroup with a grid covering the whole
 // tensor (measured faster than fewer, looping workgroups); non-temporal
 // loads and stores for the streaming data (1.5-1.8x faster than cached).
-// Flat dequants, and both passes of the two-pass casts, over 1-4 M lane
-// vectors (8-32 M 16-bit elements, 4-16 M fp32 elements) take K = 4 or 8
-// instead (pick_flat_k), which brings their grid to about one dispatch round.
+// Flat dequants and casts (one-pass, and both passes of the two-pass ones)
+// over 1-4 M lane vectors (8-32 M 16-bit elements, 4-16 M fp32 elements)
+// take K = 4 or 8 instead (pick_flat_k), which brings their grid to about one
+// dispatch round.  The reduce step and the packed dequant (a grid over W
+// slots) keep K = 2.
 // The amax passes are the exception: their grid is capped at kAmaxGrid
 // workgroups that loop over chunks.  In the stand-alone amax every workgroup
 // ends in one atomic max on a single word, and those serialise across the 8
@@ -118,17 +120,17 @@ template <int DT, int FMT> struct RunGroup128 {
     }
 };
 
-// cached: ordinary loads and stores instead of non-temporal ones, for a
-// cast pass whose input was just written by the previous kernel (the
-// reduce step's re-cast: 90.4 us against 93.1 us for 8 x 2^25 e5m2 chunks)
-// The cast pass takes the same sub-steps per chunk as the amax pass before it
-// (pick_flat_k over the tensor's lane vectors, in both), so that chunk c is
-// cast by workgroup c on the XCD whose L2 the amax pass loaded it into (amax
-// workgroup c mod 1024).  A fatter cast chunk over K = 2 amax chunks broke
-// that pairing (bf16 [4096, 4096]: 16.5 us against 15.1 us); fatter chunks in
-// both passes keep it and gain (14.7 against 15.3 us; fp32 26.3 against 27.2).
-// The reduce step's re-cast (cached) folds amax slots, not partials, and
-// keeps K = 2.
+// The cast pass of a two-pass cast.  It takes the same sub-steps per chunk
+// as the amax pass before it (pick_flat_k over the tensor's lane vectors, in
+// both), so that chunk c is cast by workgroup c on the XCD whose L2 the amax
+// pass loaded it into (amax workgroup c mod 1024).  A fatter cast chunk over
+// K = 2 amax chunks broke that pairing (bf16 [4096, 4096]: 16.5 us against
+// 15.1 us); fatter chunks in both passes keep it and gain (14.7 against
+// 15.3 us; fp32 26.3 against 27.2).
+// cached: ordinary loads and stores instead of non-temporal ones, for the
+// reduce step's re-cast, whose input the sum pass has just written (90.4 us
+// against 93.1 us for 8 x 2^25 e5m2 chunks); it folds amax slots, not
+// partials, and keeps K = 2.
 template <int DT, int FMT> struct RunTensorCast {
     static void run(const void* x, int64_t n, const uint32_t* partial, int np, int pstride, uint8_t* q, float* sinv,
                     bool cached, hipStream_t st) {
@@ -152,9 +154,11 @@ template <int DT, int FMT> struct RunTensorCast {
 template <int DT, int FMT> struct RunCastGivenAmax {
     static void run(const void* x, int64_t n, const float* amax, uint8_t* q, float* scale_out, hipStream_t st) {
         constexpr int VE = LaneVE<DT>::value;
-        if (al(x, 16) && al(q, 4)) {
-            const int64_t chunks = (n / VE + kFlatK * 256 - 1) / (kFlatK * 256);
-            k_cast_given_amax<DT, FMT, true, kFlatK, kNT><<<grid(chunks), kThreads, 0, st>>>(x, n, amax, q, scale_out);
+        if (al(x, 16) && al(q, 4)) {   // bf16 [4096, 4096]: 11.4 us with K = 4 against 12.1 with K = 2
+            launch_k(n / VE, [&](auto K, unsigned nb) {
+                k_cast_given_amax<DT, FMT, true, decltype(K)::value, kNT><<<nb, kThreads, 0, st>>>(x, n, amax, q,
+                                                                                                   scale_out);
+            });
         } else {
             k_cast_given_amax<DT, FMT, false, kFlatK, kNT><<<grid((n + 255) / 256), kThreads, 0, st>>>(x, n, amax, q,
                                                                                                        scale_out);
@@ -286,9 +290,10 @@ template <int DT> void run_pipeline_cast(const void* x, int64_t n, const uint32_
 template <int YDT> void run_dequant_pipeline(const uint8_t* q, int64_t n, const float* sinv, const int32_t* fmt,
                                              void* y, hipStream_t st) {
     constexpr int VE = LaneVE<YDT>::value;
-    if (al(q, 4) && al(y, 16)) {
-        const unsigned nb = grid((n / VE + kFlatK * 256 - 1) / (kFlatK * 256));
-        k_dequant_pipeline<YDT, true, kFlatK, kNT><<<nb, kThreads, 0, st>>>(q, n, sinv, fmt, y);
+    if (al(q, 4) && al(y, 16)) {   // as the per-tensor dequant: [4096, 4096] -> bf16 10.3 us against 11.6
+        launch_k(n / VE, [&](auto K, unsigned nb) {
+            k_dequant_pipeline<YDT, true, decltype(K)::value, kNT><<<nb, kThreads, 0, st>>>(q, n, sinv, fmt, y);
+        });
     } else {
         k_dequant_pipeline<YDT, false, kFlatK, kNT><<<grid((n + 255) / 256), kThreads, 0, st>>>(q, n, sinv, fmt, y);
     }

@@ -58,6 +58,32 @@ def test_fsdp_hook_parts(fmt, dtype):
             assert_hp_equal(host(y), oracle.dequant_div_scale(wq, fmt, wsc[0], ydt), ydt, f"div dequant {ydt}")
 
 
+@pytest.mark.parametrize("dtype,n", [("bf16", 9_000_005), ("f32", 12_000_003), ("f16", 30_000_001)])
+def test_fsdp_hook_fat_chunks(dtype, n):
+    """Shard sizes whose one-pass cast and division dequant take 4 or 8
+    sub-steps per chunk, with ragged tails."""
+    rng = np.random.Generator(np.random.PCG64(n))
+    x = (rng.standard_normal(n) * 7.0).astype(np.float32)
+    xh = W.to_bf16_bits(x) if dtype == "bf16" else (x.astype(np.float16).view(np.uint16) if dtype == "f16" else x)
+    a = G.empty(1, dtype=torch.float32, device="cuda:0")
+    fq.fp8q_amax_guarded(dev(xh, dtype), a)
+    torch.cuda.synchronize()
+    g = np.float32(oracle.amax_guarded(xh, dtype))
+    assert host(a)[0] == g
+    q = G.empty(n, dtype=torch.uint8, device="cuda:0")
+    sc = G.empty(1, dtype=torch.float32, device="cuda:0")
+    print(f"[case] cast_with_amax fat chunks {dtype} n={n}", flush=True)
+    fq.fp8q_cast_with_amax(dev(xh, dtype), a, q, sc, "e5m2")
+    torch.cuda.synchronize()
+    wq, wsc = oracle.cast_with_amax(xh, dtype, "e5m2", g)
+    assert_fp8_equal(host(q), wq, "e5m2", "fat cast_with_amax q")
+    assert_f32_equal(host(sc), wsc, "fat cast_with_amax scale")
+    y = empty_hp(n, "bf16")
+    fq.fp8q_dequant_div_scale(q, sc, y, "e5m2")
+    torch.cuda.synchronize()
+    assert_hp_equal(host(y), oracle.dequant_div_scale(wq, "e5m2", wsc[0], "bf16"), "bf16", "fat div dequant")
+
+
 def test_cast_with_too_small_amax_saturates():
     """An amax below the shard's own max: products leave the fp8 range and
     saturate (the hardware convert alone would give NaN/inf)."""
