@@ -259,3 +259,39 @@ def test_valid_calls_reach_the_launchers():
         {"dequant_sum": 1, "tensor_cast": 1}
     assert calls(L.fp8q_dequant_sum_requant, None, E5, 4, 0, s, 1, None, BF16, None, w, ws, None) == \
         {"fill_f32": 1}
+
+
+@pytest.mark.skipif(not STUBS, reason="needs the launcher-stub build of the ABI layer (run by test_sanitizers.py)")
+def test_fuzz_validation():
+    """Random calls of every entry point with sizes at and beyond the int64
+    limits, NULL, odd and far-apart fake pointers, and out-of-range enum values.
+    Every call must return one of the documented status codes; under the
+    sanitizer build any undefined behaviour in the validation arithmetic aborts
+    the process, and a call that reaches a launcher with a broken precondition
+    aborts in the stub."""
+    import numpy as np
+    rng = np.random.Generator(np.random.PCG64(77))
+    sizes = [0, 1, 2, 3, 7, 8, 127, 128, 129, 4096, 2 ** 31 - 1, 2 ** 31, 2 ** 32 + 1, 2 ** 40, 2 ** 62,
+             2 ** 63 - 1, -1, -2, -(2 ** 63)]
+    ptrs = [None, A, A + 1, A + 2, A + 4, A + 8, A + 16, A + 4096, A + (1 << 20), A + (1 << 40),
+            2 ** 64 - 4096, 4]
+    enums = [0, 1, 2, 3, -1, 7, 2 ** 31 - 1, -(2 ** 31)]
+    codes = {fq.OK, fq.EINVAL, fq.EDTYPE, fq.ESHAPE, fq.EALIGN, fq.EHIP}
+    for name in fq.ABI_FUNCTIONS:
+        fn = getattr(L, name)
+        if name in ("fp8q_abi_version", "fp8q_status_str", "fp8q_per_tensor_workspace_bytes"):
+            continue
+        for _ in range(1000):
+            args = []
+            for t in fn.argtypes:
+                if t is ctypes.c_void_p:
+                    p = ptrs[int(rng.integers(0, len(ptrs)))]
+                    args.append(None if p is None else P(p))
+                elif t is ctypes.c_int64:
+                    args.append(sizes[int(rng.integers(0, len(sizes)))] if rng.random() < 0.8
+                                else int(rng.integers(0, 1 << 20)))
+                else:
+                    args.append(enums[int(rng.integers(0, len(enums)))] if rng.random() < 0.5
+                                else int(rng.integers(0, 3)))
+            args[-1] = None                                  # the stream
+            assert fn(*args) in codes, (name, args)
