@@ -430,17 +430,24 @@ def _other_rows(fq, W, np, torch, dev, st, iters, log, HE, act, roundtrip):
           Ra * Ca, lambda: fq.fp8q_dequant_per_group128(qa8, sa8, ya8, "e4m3fn", stream=st))
     del ya8
     # the same cast from views that start two elements into their buffers
-    # (4-byte aligned, not 16): the pair kernel, one wavefront per 128-group
-    # with two bf16 per lane -- the shape the per-group cast is often described
-    # with, next to the 16-lane / 16-byte k_group128 of the headline row
+    # (x 4-byte aligned, not 16; q 2-byte aligned): the shifted kernel, whose
+    # aligned 16-byte loads are re-formed into each lane's elements by a
+    # cross-lane shuffle and whose aligned stores straddle two lanes' codes
     xo = torch.empty(Ra * Ca + 2, dtype=torch.bfloat16, device=dev)
     xo[2:].copy_(act.reshape(-1))
     qo = torch.empty(Ra * Ca + 2, dtype=torch.uint8, device=dev)
     xv, qv = xo[2:].view(Ra, Ca), qo[2:].view(Ra, Ca)
-    timed("group128_cast_bf16_e4m3fn_16384x7168 (x, q two elements into their buffers: k_group128_pair, "
-          "one wavefront per group, 4-byte loads)", Ra * Ca * 3 + Ra * (Ca // 128) * 4, Ra * Ca,
+    timed("group128_cast_bf16_e4m3fn_16384x7168 (x, q two elements into their buffers: k_group128_shift, "
+          "aligned loads re-formed by a lane shuffle)", Ra * Ca * 3 + Ra * (Ca // 128) * 4, Ra * Ca,
           lambda: fq.fp8q_cast_per_group128(xv, qv, sa8, "e4m3fn", stream=st))
-    del xo, qo, xv, qv, qa8, sa8
+    del xo, qo, xv, qv
+    # the same cast in the one-wavefront-per-group shape (64 lanes x 2 bf16,
+    # 4-byte loads, 2-byte stores) on the aligned buffers, beside the
+    # 16-lane / 16-byte k_group128 of the headline row
+    timed("group128_cast_bf16_e4m3fn_16384x7168 (one wavefront per group, 64 lanes x 2 bf16: "
+          "fp8q_cast_per_group128_wave64)", Ra * Ca * 3 + Ra * (Ca // 128) * 4, Ra * Ca,
+          lambda: fq.fp8q_cast_per_group128_wave64(act, qa8, sa8, "e4m3fn", stream=st))
+    del qa8, sa8
 
     # pipeline p2p cast of the activation (bf16 [16384, 7168]) with the format
     # chosen on the device, and back to bf16

@@ -54,6 +54,7 @@ def _load(path: str = LIB_PATH):
         "fp8q_cast_per_tensor_noalloc": (I, [P, I, I64, I, P, P, P]),
         "fp8q_cast_per_channel": (I, [P, I, I64, I64, I, P, P, P]),
         "fp8q_cast_per_group128": (I, [P, I, I64, I64, I, P, P, P]),
+        "fp8q_cast_per_group128_wave64": (I, [P, I, I64, I64, I, P, P, P]),
         "fp8q_dequant_per_tensor": (I, [P, I, I64, P, P, I, P]),
         "fp8q_dequant_per_channel": (I, [P, I, I64, I64, P, P, I, P]),
         "fp8q_dequant_per_group128": (I, [P, I, I64, I64, P, P, I, P]),
@@ -78,6 +79,7 @@ def _load(path: str = LIB_PATH):
 lib = _load()
 ABI_FUNCTIONS = ("fp8q_abi_version", "fp8q_status_str", "fp8q_per_tensor_workspace_bytes", "fp8q_amax",
                  "fp8q_cast_per_tensor", "fp8q_cast_per_channel", "fp8q_cast_per_group128",
+                 "fp8q_cast_per_group128_wave64",
                  "fp8q_dequant_per_tensor", "fp8q_dequant_per_channel", "fp8q_dequant_per_group128",
                  "fp8q_weight_dequant_block128", "fp8q_dequant_sum", "fp8q_dequant_sum_requant",
                  "fp8q_amax_guarded", "fp8q_cast_with_amax", "fp8q_dequant_div_scale",
@@ -217,14 +219,24 @@ def fp8q_cast_per_channel(x, q, scale_inv, fmt="e4m3fn", stream=None) -> None:
                                      _dev(scale_inv, "scale_inv"), _stream(x, stream)), "fp8q_cast_per_channel")
 
 
-def fp8q_cast_per_group128(x, q, scale_inv, fmt="e4m3fn", stream=None) -> None:
+def _group128_cast(name, x, q, scale_inv, fmt, stream) -> None:
     f = _fp8(q, fmt, "q")
     rows, cols = _rows_cols(x)
     if q.numel() != x.numel() or scale_inv.dtype != torch.float32 or \
             (cols % 128 == 0 and scale_inv.numel() != rows * (cols // 128)):
-        raise ValueError("fp8q_cast_per_group128: q must match x and scale_inv must be float32[rows, cols/128]")
-    _check(lib.fp8q_cast_per_group128(_dev(x, "x"), _hp_dtype(x, "x"), rows, cols, f, _dev(q, "q"),
-                                      _dev(scale_inv, "scale_inv"), _stream(x, stream)), "fp8q_cast_per_group128")
+        raise ValueError(f"{name}: q must match x and scale_inv must be float32[rows, cols/128]")
+    _check(getattr(lib, name)(_dev(x, "x"), _hp_dtype(x, "x"), rows, cols, f, _dev(q, "q"),
+                              _dev(scale_inv, "scale_inv"), _stream(x, stream)), name)
+
+
+def fp8q_cast_per_group128(x, q, scale_inv, fmt="e4m3fn", stream=None) -> None:
+    _group128_cast("fp8q_cast_per_group128", x, q, scale_inv, fmt, stream)
+
+
+def fp8q_cast_per_group128_wave64(x, q, scale_inv, fmt="e4m3fn", stream=None) -> None:
+    """The same cast in the one-wavefront-per-group kernel shape (for
+    measurement; x aligned to two elements, q to 2 bytes)."""
+    _group128_cast("fp8q_cast_per_group128_wave64", x, q, scale_inv, fmt, stream)
 
 
 def fp8q_dequant_per_tensor(q, scale_inv, y, fmt=None, stream=None) -> None:

@@ -274,6 +274,22 @@ fp8q_status_t fp8q_cast_per_group128(const void* x, fp8q_dtype_t xdtype, int64_t
     return launched();
 }
 
+fp8q_status_t fp8q_cast_per_group128_wave64(const void* x, fp8q_dtype_t xdtype, int64_t rows, int64_t cols,
+                                            fp8q_fmt_t fmt, uint8_t* q, float* scale_inv, void* stream) {
+    if (!valid_dtype(xdtype) || !valid_fmt(fmt)) return FP8Q_EDTYPE;
+    if (rows < 0 || cols < 0) return FP8Q_EINVAL;
+    if (cols % 128 != 0) return FP8Q_ESHAPE;
+    int64_t groups;
+    if (!mul_ok(rows, cols / 128, &groups)) return FP8Q_EINVAL;
+    int64_t n;
+    fp8q_status_t st = check_2d(x, xdtype, rows, cols, fmt, q, scale_inv, groups, &n);
+    if (st != FP8Q_OK) return st;
+    if (n == 0) return FP8Q_OK;
+    if (!aligned(x, 2 * esize(xdtype)) || !aligned(q, 2)) return FP8Q_EALIGN;
+    fp8q::launch_group128_cast_wave64(x, xdtype, groups, fmt, q, scale_inv, S(stream));
+    return launched();
+}
+
 fp8q_status_t fp8q_dequant_per_tensor(const uint8_t* q, fp8q_fmt_t fmt, int64_t n, const float* scale_inv, void* y,
                                       fp8q_dtype_t ydtype, void* stream) {
     if (n < 0) return FP8Q_EINVAL;

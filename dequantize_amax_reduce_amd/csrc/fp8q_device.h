@@ -27,6 +27,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fp8q_launch.h"
 
 namespace fp8q {
@@ -362,16 +364,19 @@ k_group128(const void* __restrict__ x, uint8_t* __restrict__ q, float* __restric
     }
 }
 
-// Pair path, for x aligned to two elements but not to 16 bytes (a view that
-// starts a few elements into a buffer) and q aligned to 2 bytes: one
-// wavefront per 128-group, 64 lanes x 2 consecutive elements (one 4-byte
-// load for bf16 / fp16, one 8-byte load for fp32), the group max by a
-// 64-lane DPP reduction with no LDS round trip, and one 2-byte store of the
-// pair's codes per lane.  A wave takes G consecutive groups per trip, all
-// loaded before the first is converted.  This is the one-wavefront-per-group
-// shape; on the activation workload it takes about 100 us against 56 us for
-// k_group128's 16 lanes x 8 elements with 16-byte loads, so it only serves
-// inputs the 16-byte path cannot take.
+// The per-128-group cast (DeepEP "5 Utils", per_token_cast_to_fp8) in the
+// one-wavefront-per-group shape (a 64-lane wave per group, 2 elements per
+// lane): one 4-byte load per lane
+// for bf16 / fp16 (8-byte for fp32), the group max by a 64-lane DPP reduction
+// with no LDS round trip, and one 2-byte store of the pair's codes per lane.
+// A wave takes G consecutive groups per trip, all loaded before the first is
+// converted.  x must be aligned to two elements and q to 2 bytes.  Results are
+// identical to k_group128's; on the activation workload it takes about 108 us
+// against 56 us (4-byte loads carry a quarter of the bytes per memory
+// instruction, and 2-byte stores write 23 % more than their algorithmic
+// bytes), so fp8q_cast_per_group128 never uses it: it is reached only through
+// fp8q_cast_per_group128_wave64, which keeps the shape measurable beside the
+// kernel chosen.
 template <int DT, int FMT, int G>
 __global__ void __launch_bounds__(256)
 k_group128_pair(const void* __restrict__ x, uint8_t* __restrict__ q, float* __restrict__ sinv_out, int64_t groups) {
@@ -422,23 +427,173 @@ k_group128_pair(const void* __restrict__ x, uint8_t* __restrict__ q, float* __re
     }
 }
 
-// Unaligned path: one wavefront per group, two elements per lane,
-// element-wise loads and byte stores; correct for any alignment of x (to its
-// element size) and q.
-template <int DT, int FMT>
+// Shifted path, for x aligned only to its element size and q to nothing (a
+// view that starts a few elements into a buffer).  The lanes keep
+// k_group128's shape (LPG lanes x VE elements per group, one 16-byte load and
+// one VE-byte store each) and every global access stays aligned.  Each wave
+// takes a contiguous span of K x 64 lane vectors (K sub-steps of 64):
+//  - load side: lane t loads the 16-byte-aligned vector holding the start of
+//    its VE elements and takes the next lane's leading dwords by a whole-wave
+//    DPP shift; lane 63 takes them from lane 0's vector of the next sub-step
+//    (a readlane), and at the span's last sub-step from one extra load.  A
+//    byte shift (v_alignbyte) then forms the lane's elements.
+//  - store side: lane t writes the VE-aligned word that ends inside its codes,
+//    the previous lane's trailing bytes (DPP shift; for lane 0, lane 63's codes
+//    of the previous sub-step) then its own leading bytes.  Only the span's
+//    first lane writes just its own bytes, and only the span's last lane (or
+//    the lane holding the tensor's last vector) writes its trailing bytes on
+//    its own, in the widest aligned pieces that fit.
+// The two 16-byte vectors that straddle either end of x are read element by
+// element over the bytes x holds, so nothing outside x or q is touched.
+// XDW = (x mod 16) / 4 is a template argument so that the dword selection is
+// fixed at compile time; the byte shift within a dword (x mod 4: 0, or 2 for
+// the 16-bit types) and q's offset from a VE-byte boundary are runtime values,
+// uniform across the grid.
+
+// x's 16-byte-aligned vector j (at xa + 16 j), with the bytes outside
+// [lo, hi) (offsets from xa) read as zero and never touched.  Lanes beyond the
+// tensor take all zeros.
+template <int ESZ, bool NT>
+__device__ __forceinline__ v4u aligned_vec16(const char* xa, int64_t j, int64_t lo, int64_t hi) {
+    const int64_t o = j * 16;
+    if (o >= lo && o + 16 <= hi) return ld16<NT>(xa + o);
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    if (o < hi && o + 16 > lo) {
+#pragma unroll
+        for (int e = 0; e < 16; e += ESZ) {
+            if (o + e >= lo && o + e + ESZ <= hi) {
+                if constexpr (ESZ == 4) w[e >> 2] = *(const uint32_t*)(xa + o + e);
+                else w[e >> 2] |= (uint32_t)*(const uint16_t*)(xa + o + e) << (8 * (e & 3));
+            }
+        }
+    }
+    return v4u{w[0], w[1], w[2], w[3]};
+}
+
+// bytes [lo, hi) of w (little-endian) to the W-byte-aligned word at p, in
+// naturally aligned pieces of 4, 2 and 1 bytes
+template <typename W>
+__device__ __forceinline__ void store_bytes(uint8_t* p, W w, int lo, int hi) {
+    for (int b = lo; b < hi;) {
+        if ((b & 3) == 0 && b + 4 <= hi) {
+            *(uint32_t*)(p + b) = (uint32_t)(w >> (8 * b));
+            b += 4;
+        } else if ((b & 1) == 0 && b + 2 <= hi) {
+            *(uint16_t*)(p + b) = (uint16_t)(w >> (8 * b));
+            b += 2;
+        } else {
+            p[b] = (uint8_t)(w >> (8 * b));
+            b += 1;
+        }
+    }
+}
+
+// whole-wave DPP lane shifts (bound_ctrl off: the lane with no source keeps 0)
+__device__ __forceinline__ uint32_t from_next_lane(uint32_t v) {   // lane t <- lane t + 1 (wave_shl:1)
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x130, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t from_prev_lane(uint32_t v) {   // lane t <- lane t - 1 (wave_shr:1)
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x138, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t lane_value(uint32_t v, int lane) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
+}
+
+template <int DT, int FMT, int K, int XDW>
 __global__ void __launch_bounds__(256)
-k_group128_wave(const void* __restrict__ x, uint8_t* __restrict__ q, float* __restrict__ sinv_out, int64_t groups) {
+k_group128_shift(const void* __restrict__ x, uint8_t* __restrict__ q, float* __restrict__ sinv_out, int64_t groups) {
+    constexpr int VE = LaneVE<DT>::value;
+    constexpr int ESZ = ESize<DT>::value;
+    constexpr int LPG = 128 / VE;
+    constexpr int GPW = 64 / LPG;                   // groups per wave sub-step
+    constexpr int CH = K * 4 * GPW;                 // groups per workgroup chunk
+    using Word = typename std::conditional<VE == 8, uint64_t, uint32_t>::type;
+    const int mx = (int)((uintptr_t)x & 15);        // 4 * XDW + xsb
+    const int xsb = mx & 3;
+    const int mq = (int)((uintptr_t)q & (VE - 1));
+    const char* xa = (const char*)x - mx;            // 16-byte aligned
+    uint8_t* qa = q - mq;                            // VE-byte aligned
+    const int64_t nvec = groups * LPG;               // x's lane vectors (16 bytes each)
+    const int64_t xhi = mx + nvec * 16;              // x's bytes are [mx, xhi) from xa
     const int lane = threadIdx.x & 63;
-    const int64_t waves = (int64_t)gridDim.x * (blockDim.x / 64);
-    for (int64_t g = (int64_t)blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64; g < groups; g += waves) {
-        const int64_t e0 = g * 128 + 2 * lane;
-        const uint32_t m = max_lanes<64>(umax(absbits1<DT>(x, e0), absbits1<DT>(x, e0 + 1)));
-        float scale, sinv;
-        group_scale<FMT>(m, scale, sinv);
-        const uint32_t w = enc4<FMT>(load1<DT>(x, e0) * scale, load1<DT>(x, e0 + 1) * scale, 0.0f, 0.0f);
-        q[e0] = (uint8_t)(w & 0xFF);
-        q[e0 + 1] = (uint8_t)((w >> 8) & 0xFF);
-        if (lane == 0) sinv_out[g] = sinv;
+    const int lig = lane % LPG;
+    const int64_t nchunks = (groups + CH - 1) / CH;
+    for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+        const int64_t g0 = c * CH + (int64_t)(threadIdx.x >> 6) * (K * GPW);   // the wave's first group
+        const int64_t v0 = g0 * LPG;                                             // and first lane vector
+        v4u a[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) a[k] = aligned_vec16<ESZ, true>(xa, v0 + k * 64 + lane, mx, xhi);
+        v4u e = v4u{0u, 0u, 0u, 0u};
+        if (mx != 0 && lane == 63) e = aligned_vec16<ESZ, true>(xa, v0 + K * 64, mx, xhi);
+        uint32_t plo = 0u, phi = 0u;   // lane 63's codes at the previous sub-step
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            // every lane is active here
+            uint32_t s[8] = {a[k].x, a[k].y, a[k].z, a[k].w, 0u, 0u, 0u, 0u};
+            if (mx != 0) {   // uniform
+#pragma unroll
+                for (int d = 0; d <= XDW; ++d) {
+                    const uint32_t nx = from_next_lane(s[d]);   // straight-line, every lane active
+                    uint32_t last = e[d];
+                    if (k + 1 < K) last = lane_value(a[(k + 1) % K][d], 0);   // k is a constant here
+                    s[4 + d] = lane == 63 ? last : nx;
+                }
+            }
+            HpVec<DT> v;
+            v.r = v4u{__builtin_amdgcn_alignbyte(s[XDW + 1], s[XDW + 0], xsb),
+                      __builtin_amdgcn_alignbyte(s[XDW + 2], s[XDW + 1], xsb),
+                      __builtin_amdgcn_alignbyte(s[XDW + 3], s[XDW + 2], xsb),
+                      __builtin_amdgcn_alignbyte(s[XDW + 4], s[XDW + 3], xsb)};
+            const int64_t g = g0 + k * GPW + lane / LPG;
+            Word cw = 0;
+            if (g < groups) {  // uniform within the LPG lanes of a group; valid lanes are a prefix
+                const uint32_t amax = max_lanes<LPG>(v.absmax_bits());
+                float scale, sinv;
+                group_scale<FMT>(amax, scale, sinv);
+                float f[VE];
+                v.widen(f);
+                if constexpr (VE == 8) {
+                    cw = (uint64_t)enc4<FMT>(f[0] * scale, f[1] * scale, f[2] * scale, f[3] * scale) |
+                         ((uint64_t)enc4<FMT>(f[4] * scale, f[5] * scale, f[6] * scale, f[7] * scale) << 32);
+                } else {
+                    cw = enc4<FMT>(f[0] * scale, f[1] * scale, f[2] * scale, f[3] * scale);
+                }
+                const int64_t vi = v0 + k * 64 + lane;  // this lane's vector; its codes are q[VE vi, VE vi + VE)
+                uint8_t* wq = qa + vi * VE;             // the aligned word holding the first of them
+                if (mq == 0) {
+                    if constexpr (VE == 8) st8<true>(wq, v2u{(uint32_t)cw, (uint32_t)(cw >> 32)});
+                    else st4<true>(wq, cw);
+                } else {
+                    // the previous lane's codes (lane t - 1 is valid whenever lane t
+                    // is).  The DPP shifts run in straight-line code, outside any
+                    // condition on the lane: a shift executed under a mask that
+                    // disables its source lane reads 0 instead of that lane.
+                    Word pw;
+                    if constexpr (VE == 8) {
+                        const uint32_t lo = from_prev_lane((uint32_t)cw), hi = from_prev_lane((uint32_t)(cw >> 32));
+                        pw = lane == 0 ? ((uint64_t)plo | ((uint64_t)phi << 32)) : ((uint64_t)lo | ((uint64_t)hi << 32));
+                    } else {
+                        const uint32_t lo = from_prev_lane(cw);
+                        pw = lane == 0 ? plo : lo;
+                    }
+                    const Word w = (Word)(cw << (8 * mq)) | (Word)(pw >> (8 * (VE - mq)));
+                    if (lane != 0 || k > 0) {
+                        if constexpr (VE == 8) st8<true>(wq, v2u{(uint32_t)w, (uint32_t)(w >> 32)});
+                        else st4<true>(wq, w);
+                    } else {
+                        store_bytes<Word>(wq, w, mq, VE);
+                    }
+                    if ((lane == 63 && k == K - 1) || vi == nvec - 1)
+                        store_bytes<Word>(wq + VE, (Word)(cw >> (8 * (VE - mq))), 0, mq);
+                }
+                if (lig == 0) sinv_out[g] = sinv;
+            }
+            if (mq != 0 && k + 1 < K) {
+                plo = lane_value((uint32_t)cw, 63);
+                if constexpr (VE == 8) phi = lane_value((uint32_t)((uint64_t)cw >> 32), 63);
+            }
+        }
     }
 }
 

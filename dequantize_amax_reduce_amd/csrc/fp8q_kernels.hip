@@ -102,21 +102,33 @@ void dispatch_fmt_ydt(int fmt, int ydt, A... a) {
     }
 }
 
-constexpr int kPairG = 8;          // groups per wave trip in the pair path
 
 template <int DT, int FMT> struct RunGroup128 {
     static void run(const void* x, int64_t groups, uint8_t* q, float* sinv, hipStream_t st) {
         constexpr int VE = LaneVE<DT>::value;
-        constexpr int ESZ = ESize<DT>::value;
+        constexpr int64_t CH = kGroupK * (256 / (128 / VE));
+        const unsigned nb = grid((groups + CH - 1) / CH);
         if (al(x, 16) && al(q, 4)) {
-            constexpr int64_t CH = kGroupK * (256 / (128 / VE));
-            k_group128<DT, FMT, kGroupK, kNT><<<grid((groups + CH - 1) / CH), kThreads, 0, st>>>(x, q, sinv, groups);
-        } else if (al(x, 2 * ESZ) && al(q, 2)) {
-            const int64_t trips = (groups + kPairG - 1) / kPairG;
-            k_group128_pair<DT, FMT, kPairG><<<grid((trips + 3) / 4), kThreads, 0, st>>>(x, q, sinv, groups);
+            k_group128<DT, FMT, kGroupK, kNT><<<nb, kThreads, 0, st>>>(x, q, sinv, groups);
         } else {
-            k_group128_wave<DT, FMT><<<grid((groups + 3) / 4), kThreads, 0, st>>>(x, q, sinv, groups);
+            // x is aligned to its element size (checked at the boundary), so
+            // x mod 16 is a whole number of elements
+            switch (((uintptr_t)x & 15) >> 2) {
+                case 0: k_group128_shift<DT, FMT, kGroupK, 0><<<nb, kThreads, 0, st>>>(x, q, sinv, groups); break;
+                case 1: k_group128_shift<DT, FMT, kGroupK, 1><<<nb, kThreads, 0, st>>>(x, q, sinv, groups); break;
+                case 2: k_group128_shift<DT, FMT, kGroupK, 2><<<nb, kThreads, 0, st>>>(x, q, sinv, groups); break;
+                default: k_group128_shift<DT, FMT, kGroupK, 3><<<nb, kThreads, 0, st>>>(x, q, sinv, groups); break;
+            }
         }
+    }
+};
+
+// the one-wavefront-per-group variant (x aligned to two elements, q to 2 bytes)
+constexpr int kPairG = 8;          // groups per wave trip
+template <int DT, int FMT> struct RunGroup128Wave64 {
+    static void run(const void* x, int64_t groups, uint8_t* q, float* sinv, hipStream_t st) {
+        const int64_t trips = (groups + kPairG - 1) / kPairG;
+        k_group128_pair<DT, FMT, kPairG><<<grid((trips + 3) / 4), kThreads, 0, st>>>(x, q, sinv, groups);
     }
 };
 
@@ -483,6 +495,11 @@ void launch_channel_cast(const void* x, int dt, int64_t rows, int64_t cols, int 
 void launch_group128_cast(const void* x, int dt, int64_t groups, int fmt, uint8_t* q, float* sinv,
                           hipStream_t st) {
     dispatch_dt_fmt<RunGroup128>(dt, fmt, x, groups, q, sinv, st);
+}
+
+void launch_group128_cast_wave64(const void* x, int dt, int64_t groups, int fmt, uint8_t* q, float* sinv,
+                                 hipStream_t st) {
+    dispatch_dt_fmt<RunGroup128Wave64>(dt, fmt, x, groups, q, sinv, st);
 }
 
 void launch_dequant_flat(int mode, const uint8_t* q, int fmt, int64_t n, const float* sinv, void* y, int ydt,

@@ -59,6 +59,9 @@ void launch_tensor_cast(const void* x, int dt, int64_t n, int fmt, const uint32_
 void launch_channel_cast(const void* x, int dt, int64_t rows, int64_t cols, int fmt, uint8_t* q, float* sinv,
                          hipStream_t st);
 void launch_group128_cast(const void* x, int dt, int64_t groups, int fmt, uint8_t* q, float* sinv, hipStream_t st);
+// the one-wavefront-per-group variant; x aligned to two elements, q to 2 bytes
+void launch_group128_cast_wave64(const void* x, int dt, int64_t groups, int fmt, uint8_t* q, float* sinv,
+                                 hipStream_t st);
 // mode 0: per-tensor scale; mode 2: per-128-group scale over a flat [rows * cols] with cols % 128 == 0;
 // mode 3: per-tensor division by sinv[0] (a scale, not its inverse)
 void launch_dequant_flat(int mode, const uint8_t* q, int fmt, int64_t n, const float* sinv, void* y, int ydt,

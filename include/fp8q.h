@@ -142,6 +142,18 @@ fp8q_status_t fp8q_cast_per_group128(const void* x, fp8q_dtype_t xdtype, int64_t
                                      uint8_t* q, float* scale_inv, void* stream);
 
 /*
+ * The same per-128-group cast computed in another kernel shape, one 64-lane
+ * wavefront per group with two elements per lane (4-byte loads, 2-byte code
+ * stores), kept so that the shape can be measured beside the kernel that
+ * fp8q_cast_per_group128 uses; the results are identical.  On MI355X it is
+ * about half as fast as fp8q_cast_per_group128.  Arguments, layout and errors
+ * as fp8q_cast_per_group128, and also: x not aligned to two elements or q not
+ * to 2 bytes -> FP8Q_EALIGN.
+ */
+fp8q_status_t fp8q_cast_per_group128_wave64(const void* x, fp8q_dtype_t xdtype, int64_t rows, int64_t cols,
+                                            fp8q_fmt_t fmt, uint8_t* q, float* scale_inv, void* stream);
+
+/*
  * Per-tensor dequant (ColossalAI fp8.py, cast_from_fp8, per-tensor):
  *   y[i] = ydtype(fp32(q[i]) * scale_inv[0]) -- the binary32 product rounded
  * once more to bf16/fp16 when ydtype is not F32.  n == 0 is a no-op.

@@ -22,7 +22,7 @@ Count g_counts[] = {{"fill_f32", 0},         {"amax", 0},          {"amax_partia
                     {"cast_given_amax", 0},  {"dequant_packed", 0}, {"pipeline_cast", 0}, {"dequant_pipeline", 0},
                     {"tensor_cast", 0},      {"channel_cast", 0},  {"group128_cast", 0}, {"dequant_flat", 0},
                     {"dequant_rows", 0},     {"block128", 0},      {"dequant_sum", 0},
-                    {"scratch_words", 0}};
+                    {"scratch_words", 0},    {"group128_cast_wave64", 0}};
 
 void hit(const char* name) {
     for (Count& c : g_counts)
@@ -122,6 +122,13 @@ void launch_channel_cast(const void* x, int dt, int64_t rows, int64_t cols, int 
 void launch_group128_cast(const void* x, int dt, int64_t groups, int fmt, uint8_t* q, float* sinv, hipStream_t) {
     need(x && dt_ok(dt) && groups > 0 && fmt_ok(fmt) && q && sinv);
     hit("group128_cast");
+}
+
+void launch_group128_cast_wave64(const void* x, int dt, int64_t groups, int fmt, uint8_t* q, float* sinv,
+                                 hipStream_t) {
+    need(x && dt_ok(dt) && groups > 0 && fmt_ok(fmt) && q && sinv);
+    need((uintptr_t)x % (dt == fp8q::kF32 ? 8 : 4) == 0 && (uintptr_t)q % 2 == 0);
+    hit("group128_cast_wave64");
 }
 
 void launch_dequant_flat(int mode, const uint8_t* q, int fmt, int64_t n, const float* sinv, void* y, int ydt,

@@ -58,6 +58,20 @@ def test_group128_errors():
     assert f(None, BF16, 5, 0, E4, None, None, None) == fq.OK
 
 
+def test_group128_wave64_errors():
+    """The one-wavefront-per-group variant validates like the group cast and
+    also needs x aligned to two elements and q to 2 bytes."""
+    f = L.fp8q_cast_per_group128_wave64
+    assert f(P(A), BF16, 4, 100, E4, P(A + 4096), P(A + 8192), None) == fq.ESHAPE
+    assert f(P(A), 7, 4, 128, E4, P(A + 4096), P(A + 8192), None) == fq.EDTYPE
+    assert f(None, BF16, 4, 128, E4, P(A + 4096), P(A + 8192), None) == fq.EINVAL
+    assert f(P(A + 2), BF16, 4, 128, E4, P(A + 4096), P(A + 8192), None) == fq.EALIGN   # one bf16 in
+    assert f(P(A + 4), F32, 4, 128, E4, P(A + 4096), P(A + 8192), None) == fq.EALIGN    # one fp32 in
+    assert f(P(A), BF16, 4, 128, E4, P(A + 4097), P(A + 8192), None) == fq.EALIGN       # q odd
+    assert f(None, BF16, 0, 128, E4, None, None, None) == fq.OK
+    assert f(P(A + 1), BF16, 0, 128, E4, P(A + 4097), P(A + 8192), None) == fq.EALIGN
+
+
 def test_tensor_and_channel_errors():
     t = L.fp8q_cast_per_tensor
     assert t(P(A), BF16, 16, E4, P(A + 4096), P(A + 8192), None, None) == fq.EINVAL       # no workspace
@@ -226,12 +240,16 @@ def test_valid_calls_reach_the_launchers():
         assert fn(*args) == fq.OK, fn.__name__
         names = ("fill_f32", "amax", "amax_partials", "guard_amax", "cast_given_amax", "dequant_packed",
                  "pipeline_cast", "dequant_pipeline", "tensor_cast", "channel_cast", "group128_cast",
-                 "dequant_flat", "dequant_rows", "block128", "dequant_sum", "scratch_words")
+                 "dequant_flat", "dequant_rows", "block128", "dequant_sum", "scratch_words",
+                 "group128_cast_wave64")
         return {k: L.fp8q_stub_count(k.encode()) for k in names if L.fp8q_stub_count(k.encode())}
 
     x, q, s, y, ws, w = P(A), P(A + (1 << 20)), P(A + (2 << 20)), P(A + (3 << 20)), P(A + (4 << 20)), P(A + (5 << 20))
     assert calls(L.fp8q_cast_per_group128, x, BF16, 4, 256, E4, q, s, None) == {"group128_cast": 1}
     assert calls(L.fp8q_cast_per_group128, None, BF16, 0, 256, E4, None, None, None) == {}
+    assert calls(L.fp8q_cast_per_group128_wave64, P(A + 4), BF16, 4, 256, E4, P(A + (1 << 20) + 2), s, None) == \
+        {"group128_cast_wave64": 1}
+    assert calls(L.fp8q_cast_per_group128_wave64, None, BF16, 0, 256, E4, None, None, None) == {}
     assert calls(L.fp8q_cast_per_tensor, x, F32, 16, E5, q, s, ws, None) == {"amax_partials": 1, "tensor_cast": 1}
     assert calls(L.fp8q_cast_per_tensor, None, F32, 0, E5, None, s, ws, None) == {"fill_f32": 1}
     assert calls(L.fp8q_cast_per_tensor_noalloc, x, BF16, 16, E4, q, s, None) == \

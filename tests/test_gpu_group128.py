@@ -18,17 +18,19 @@ pytestmark = pytest.mark.gpu
 FMTS = ("e4m3fn", "e5m2")
 
 
-def _gpu_group_cast(x_host, dtype, fmt, x_offset=0, q_offset=0):
-    """Run fp8q_cast_per_group128; offsets (in elements / bytes) make the
-    device pointers misaligned to exercise the unaligned kernel."""
+def _gpu_group_cast(x_host, dtype, fmt, x_offset=0, q_offset=0, fn=None):
+    """Run fp8q_cast_per_group128 (or `fn`, an entry point with the same
+    arguments); offsets (in elements / bytes) make the device pointers
+    misaligned to exercise the shifted kernel."""
     rows, cols = x_host.shape
     flat = dev(np.concatenate([np.zeros(x_offset, x_host.dtype), x_host.reshape(-1)]), dtype)
     x = flat[x_offset:].view(rows, cols)
     qbuf = G.empty(rows * cols + q_offset, dtype=torch.uint8, device="cuda:0")
     q = qbuf[q_offset:].view(rows, cols)
     s = G.empty((rows, cols // 128), dtype=torch.float32, device="cuda:0")
-    print(f"[case] group128 cast {dtype} {fmt} {rows}x{cols} x_off={x_offset} q_off={q_offset}", flush=True)
-    fq.fp8q_cast_per_group128(x, q, s, fmt)
+    fn = fn or fq.fp8q_cast_per_group128
+    print(f"[case] {fn.__name__} {dtype} {fmt} {rows}x{cols} x_off={x_offset} q_off={q_offset}", flush=True)
+    fn(x, q, s, fmt)
     torch.cuda.synchronize()
     return host(q), host(s)
 
@@ -68,15 +70,34 @@ def test_group_cast_shapes(dtype, fmt, rows, cols):
     _check_cast(_inputs(dtype, rows, cols, seed=rows * 7 + cols), dtype, fmt)
 
 
-# x offset by 1 or 3 elements, or q by an odd count: the element-wise kernel;
-# x offset by an even count but not 16-byte aligned, q even: the pair kernel
-# (one wavefront per group, two elements per lane)
+# x not 16-byte aligned or q not 4-byte aligned: the shifted kernel (aligned
+# 16-byte loads re-formed by a cross-lane shuffle and a byte shift, aligned
+# stores of words that straddle two lanes' codes)
 @pytest.mark.parametrize("x_offset,q_offset", [(1, 0), (0, 3), (3, 5), (2, 0), (2, 2), (4, 6), (2, 1)])
 @pytest.mark.parametrize("dtype", ["bf16", "f32", "f16"])
 def test_group_cast_unaligned(dtype, x_offset, q_offset):
     for fmt in FMTS:
         _check_cast(_inputs(dtype, 33, 384, seed=5), dtype, fmt, x_offset=x_offset, q_offset=q_offset)
         _check_cast(_inputs(dtype, 70, 1152, seed=6), dtype, fmt, x_offset=x_offset, q_offset=q_offset)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "f16"])
+def test_group_cast_every_misalignment(dtype):
+    """Every offset of x from a 16-byte boundary (in elements) against every
+    offset of q from an 8-byte boundary, on one group and on 99 groups (whole
+    chunks, then a ragged one), the formats alternating: each combination
+    but the aligned one takes the shifted kernel, whose first and last
+    vectors straddle the ends of x and q."""
+    esz = 4 if dtype == "f32" else 2
+    for rows, cols, seed in ((1, 128, 12), (33, 384, 11)):
+        x_host = _inputs(dtype, rows, cols, seed=seed)
+        ref = {fmt: oracle.cast_per_group128(x_host, dtype, fmt) for fmt in FMTS}
+        for xo in range(16 // esz):
+            for qo in range(8):
+                fmt = FMTS[(xo + qo) % 2]
+                q, s = _gpu_group_cast(x_host, dtype, fmt, x_offset=xo, q_offset=qo)
+                assert_fp8_equal(q, ref[fmt][0], fmt, f"q {dtype} {fmt} {rows}x{cols} x+{xo} q+{qo}")
+                assert_f32_equal(s, ref[fmt][1], f"scale_inv {dtype} {fmt} {rows}x{cols} x+{xo} q+{qo}")
 
 
 def test_group_cast_edge_values():
@@ -203,6 +224,40 @@ def test_activation_config_full_size():
     fq.fp8q_dequant_per_group128(dev(q), dev(s), y, "e4m3fn")
     torch.cuda.synchronize()
     assert_hp_equal(host(y), oracle.dequant_per_group128(q, "e4m3fn", s, "bf16"), "bf16", "activation dequant")
+
+
+def test_activation_config_full_size_shifted():
+    """The same workload with x and q two elements into their buffers (the
+    shifted kernel, as the benchmark times it), whole output against the
+    oracle."""
+    x, ch = W.activation_outlier_channels()
+    _check_cast(x, "bf16", "e4m3fn", x_offset=2, q_offset=2)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "f16"])
+@pytest.mark.parametrize("fmt", FMTS)
+def test_group_cast_wave64_variant(dtype, fmt):
+    """fp8q_cast_per_group128_wave64 (one wavefront per group, two elements
+    per lane) against the oracle, from aligned buffers and from views two
+    elements in, on one group and on ragged counts of its 8-group wave trips."""
+    for rows, cols, seed in ((1, 128, 21), (33, 384, 22), (70, 1152, 23)):
+        x_host = _inputs(dtype, rows, cols, seed=seed)
+        wq, ws = oracle.cast_per_group128(x_host, dtype, fmt)
+        for xo, qo in ((0, 0), (2, 2), (2, 6)):
+            q, s = _gpu_group_cast(x_host, dtype, fmt, x_offset=xo, q_offset=qo, fn=fq.fp8q_cast_per_group128_wave64)
+            assert_fp8_equal(q, wq, fmt, f"wave64 q {dtype} {fmt} {rows}x{cols} x+{xo} q+{qo}")
+            assert_f32_equal(s, ws, f"wave64 scale_inv {dtype} {fmt} {rows}x{cols} x+{xo} q+{qo}")
+
+
+def test_activation_config_full_size_wave64():
+    """The activation workload through the one-wavefront-per-group variant,
+    as the benchmark times it (aligned buffers), whole output against the
+    oracle."""
+    x, ch = W.activation_outlier_channels()
+    q, s = _gpu_group_cast(x, "bf16", "e4m3fn", fn=fq.fp8q_cast_per_group128_wave64)
+    wq, ws = oracle.cast_per_group128(x, "bf16", "e4m3fn")
+    assert_fp8_equal(q, wq, "e4m3fn", "wave64 activation q")
+    assert_f32_equal(s, ws, "wave64 activation scale_inv")
 
 
 def test_group_cast_empty():

@@ -4,7 +4,8 @@ its own group, tile or the tensor's amax, so the oracle computes it from the
 sampled inputs alone).  Inputs are generated on the device with seeded torch
 generators; only the samples travel to the host.
 
-- per-128-group cast and dequant of bf16 [300000, 7168] (2.15e9 elements, > 2^31)
+- per-128-group cast and dequant of bf16 [300000, 7168] (2.15e9 elements, > 2^31),
+  then the cast again from views two elements into the same buffers
 - per-tensor cast and dequant of 2^32 + 37 bf16 elements with the maximum
   planted beyond 2^32
 - 128x128 block dequant of e4m3fn [4793491, 7168] (>= 2^32 lane vectors: the
@@ -64,7 +65,24 @@ def test_group128_beyond_2_31_elements():
     assert_fp8_equal(qs, wq, "e4m3fn", "sampled rows q")
     assert_f32_equal(ss, ws, "sampled rows scale_inv")
     assert_hp_equal(ys, oracle.dequant_per_group128(wq, "e4m3fn", ws, "bf16"), "bf16", "sampled rows y")
-    _free(x, q, s, y)
+    # again from views two elements into the same buffers (one row fewer): the
+    # shifted kernel, whose vector and byte offsets pass 2^32 here
+    del y
+    R1 = R - 1
+    print(f"[case] group128 shifted [{R1}, {C}], x and q two elements in", flush=True)
+    xv = x.view(-1)[2:2 + R1 * C].view(R1, C)
+    qv = q.view(-1)[2:2 + R1 * C].view(R1, C)
+    sv = s.view(-1)[:R1 * (C // 128)].view(R1, C // 128)
+    fq.fp8q_cast_per_group128(xv, qv, sv, "e4m3fn")
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 1, R1 - 2, R1 - 1], rng.integers(0, R1, 60),
+                                     rng.integers((1 << 31) // C, R1, 8)]))
+    ri = torch.from_numpy(rows).to(DEV)
+    xs, qs, ss = _bits(xv[ri]), _bits(qv[ri]), _bits(sv[ri])
+    wq, ws = oracle.cast_per_group128(xs, "bf16", "e4m3fn")
+    assert_fp8_equal(qs, wq, "e4m3fn", "shifted sampled rows q")
+    assert_f32_equal(ss, ws, "shifted sampled rows scale_inv")
+    _free(x, q, s, xv, qv, sv)
 
 
 def test_per_tensor_beyond_2_32_elements():
