@@ -283,6 +283,7 @@ def main():
 # whose flags shape the code object (a change to any of them makes the committed
 # counter summary stale)
 KERNEL_SOURCES = ("dequantize_amax_reduce_amd/csrc/fp8q_device.h", "dequantize_amax_reduce_amd/csrc/fp8q_kernels.hip",
+                  "dequantize_amax_reduce_amd/csrc/fp8q_shift.hip", "dequantize_amax_reduce_amd/csrc/fp8q_host.h",
                   "dequantize_amax_reduce_amd/build.py")
 TRAFFIC_SUMMARY = "profiles/fp8q_kernels__bench_workloads__hbm_traffic.md"
 

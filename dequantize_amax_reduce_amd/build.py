@@ -33,7 +33,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfp8q.so")
-SOURCES = [os.path.join(CSRC, "fp8q_kernels.hip"), os.path.join(CSRC, "fp8q_abi.cpp")]
+SOURCES = [os.path.join(CSRC, f) for f in ("fp8q_kernels.hip", "fp8q_shift.hip", "fp8q_abi.cpp")]
 ARCH = "gfx950"
 
 
@@ -45,21 +45,34 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-mllvm", "-amdgpu-kernarg-preload-count=16",
-           "-Wall", "-I", INCLUDE, "-I", CSRC, *SOURCES, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
+    """Compile every source to an object, in parallel (one hipcc per
+    translation unit), then link libfp8q.so."""
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
+    flags = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+             "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-mllvm", "-amdgpu-kernarg-preload-count=16",
+             "-Wall", "-I", INCLUDE, "-I", CSRC]
     # the host pass does not know the device-only feature name; that warning is expected
     noise = "'-packed-fp32-ops' is not a recognized feature"
-    msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{msgs}")
-    if msgs.strip() and verbose:
-        print(msgs)
+
+    def run(cmd):
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed ({r.returncode}): {' '.join(cmd)}\n{msgs}")
+        if msgs.strip() and verbose:
+            print(msgs)
+
+    with tempfile.TemporaryDirectory(prefix="fp8q_build_") as tmpdir:
+        objs = [os.path.join(tmpdir, os.path.basename(src) + ".o") for src in SOURCES]
+        with ThreadPoolExecutor(len(SOURCES)) as ex:
+            for f in [ex.submit(run, [hipcc(), *flags, "-c", src, "-o", obj]) for src, obj in zip(SOURCES, objs)]:
+                f.result()
+        tmp = LIB + ".tmp%d" % os.getpid()
+        run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, LIB)
     build_example(verbose)
     return LIB

@@ -274,18 +274,20 @@ template <int FMT, int VE, bool NT> struct Fp8Vec {
     }
 };
 
-// store 16 bytes of output (4 fp32 or 8 bf16/fp16) at y + e elements
-template <int YDT, bool NT> __device__ __forceinline__ void store_out16(void* y, int64_t e, const float* p) {
+// 16 bytes of output (4 fp32 or 8 bf16/fp16) from VE binary32 values
+template <int YDT> __device__ __forceinline__ v4u pack_out16(const float* p) {
     if constexpr (YDT == kF32) {
-        st16<NT>((float*)y + e, v4u{__float_as_uint(p[0]), __float_as_uint(p[1]), __float_as_uint(p[2]),
-                                    __float_as_uint(p[3])});
+        return v4u{__float_as_uint(p[0]), __float_as_uint(p[1]), __float_as_uint(p[2]), __float_as_uint(p[3])};
     } else if constexpr (YDT == kBF16) {
-        st16<NT>((uint16_t*)y + e, v4u{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                                       pack_bf16x2(p[6], p[7])});
+        return v4u{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
     } else {
-        st16<NT>((uint16_t*)y + e, v4u{pack_f16x2(p[0], p[1]), pack_f16x2(p[2], p[3]), pack_f16x2(p[4], p[5]),
-                                       pack_f16x2(p[6], p[7])});
+        return v4u{pack_f16x2(p[0], p[1]), pack_f16x2(p[2], p[3]), pack_f16x2(p[4], p[5]), pack_f16x2(p[6], p[7])};
     }
+}
+
+// store 16 bytes of output at y + e elements
+template <int YDT, bool NT> __device__ __forceinline__ void store_out16(void* y, int64_t e, const float* p) {
+    st16<NT>((char*)y + e * ESize<YDT>::value, pack_out16<YDT>(p));
 }
 
 template <int DT> __device__ __forceinline__ float load1(const void* x, int64_t i) {
@@ -303,6 +305,288 @@ template <int YDT> __device__ __forceinline__ void store1(void* y, int64_t e, fl
     if constexpr (YDT == kF32) ((float*)y)[e] = p;
     else if constexpr (YDT == kBF16) ((uint16_t*)y)[e] = (uint16_t)(pack_bf16x2(p, 0.0f) & 0xFFFFu);
     else ((uint16_t*)y)[e] = to_f16(p);
+}
+
+// ---------------------------------------------------------------------------
+// shifted streaming: lane vectors of views that start part-way into a vector
+// ---------------------------------------------------------------------------
+// A view that starts a few elements into its buffer cannot take 16-byte
+// loads at its own lane-vector boundaries, and element-wise kernels serve it
+// at a quarter of the vector rate or less.  The shifted path keeps the vector
+// shape.  A wave streams a contiguous span of K x 64 lane vectors (K
+// sub-steps of 64); lane t of sub-step k owns logical lane vector
+// v = span + 64 k + t, whose input is IB bytes and whose output is OB bytes.
+//  - loads: every access is an aligned IB-byte vector.  Lane t loads the one
+//    holding the start of its input, takes the next lane's by a whole-wave
+//    DPP shift (wave_shl:1; lane 63 takes lane 0's of the next sub-step by a
+//    readlane, or loads one extra vector at the end of the span), and
+//    funnel-shifts the pair into its input;
+//  - stores: lane t writes the aligned OB-byte word that ends inside its
+//    output: the previous lane's trailing bytes (wave_shr:1; lane 0 takes
+//    lane 63's of the previous sub-step) then its own leading bytes.  The
+//    span's first lane writes only its own bytes, and the span's last lane
+//    (or the lane holding the last vector) also writes its trailing bytes on
+//    its own, in naturally aligned pieces; bytes past either end of the
+//    output are dropped.
+// The aligned vectors that straddle either end of the input are read
+// element by element over the bytes it holds, so nothing outside the input
+// and the output is touched.  Every DPP shift runs in straight-line code with
+// all lanes active: a shift executed under an exec mask that disables its
+// source lane reads 0 instead of that lane.
+
+template <int W> struct Dw { uint32_t d[W]; };
+
+template <int W> __device__ __forceinline__ Dw<W> dw_zero() {
+    Dw<W> r;
+#pragma unroll
+    for (int t = 0; t < W; ++t) r.d[t] = 0u;
+    return r;
+}
+
+// whole-wave DPP lane shifts (bound_ctrl off: the lane with no source keeps 0)
+__device__ __forceinline__ uint32_t from_next_lane(uint32_t v) {   // lane t <- lane t + 1 (wave_shl:1)
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x130, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t from_prev_lane(uint32_t v) {   // lane t <- lane t - 1 (wave_shr:1)
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x138, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t lane_value(uint32_t v, int lane) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
+}
+
+// bytes [off, off + 4W) of the little-endian concatenation lo, hi, for a
+// uniform 0 <= off < 4W: a dword selection (uniform branch) and a byte shift
+template <int W>
+__device__ __forceinline__ Dw<W> funnel(const Dw<W>& lo, const Dw<W>& hi, int off) {
+    uint32_t c[2 * W + 1];
+#pragma unroll
+    for (int t = 0; t < W; ++t) {
+        c[t] = lo.d[t];
+        c[W + t] = hi.d[t];
+    }
+    c[2 * W] = 0u;
+    const int sb = off & 3;
+    Dw<W> r;
+    auto pick = [&](auto D) {
+        constexpr int d0 = decltype(D)::value;
+#pragma unroll
+        for (int t = 0; t < W; ++t) r.d[t] = __builtin_amdgcn_alignbyte(c[d0 + t + 1], c[d0 + t], sb);
+    };
+    const int d0 = off >> 2;
+    if constexpr (W == 1) {
+        pick(std::integral_constant<int, 0>{});
+    } else if constexpr (W == 2) {
+        if (d0 == 0) pick(std::integral_constant<int, 0>{});
+        else pick(std::integral_constant<int, 1>{});
+    } else {
+        if (d0 == 0) pick(std::integral_constant<int, 0>{});
+        else if (d0 == 1) pick(std::integral_constant<int, 1>{});
+        else if (d0 == 2) pick(std::integral_constant<int, 2>{});
+        else pick(std::integral_constant<int, 3>{});
+    }
+    return r;
+}
+
+// the same with the dword offset d0 = off / 4 fixed at compile time
+// (sb = off mod 4)
+template <int W, int D0>
+__device__ __forceinline__ Dw<W> funnel_static(const Dw<W>& lo, const Dw<W>& hi, int sb) {
+    uint32_t c[2 * W + 1];
+#pragma unroll
+    for (int t = 0; t < W; ++t) {
+        c[t] = lo.d[t];
+        c[W + t] = hi.d[t];
+    }
+    c[2 * W] = 0u;
+    Dw<W> r;
+#pragma unroll
+    for (int t = 0; t < W; ++t) r.d[t] = __builtin_amdgcn_alignbyte(c[D0 + t + 1], c[D0 + t], sb);
+    return r;
+}
+
+// the aligned IB-byte vector j of a stream whose bytes are [lo, hi) from the
+// IB-aligned base; bytes outside [lo, hi) read as 0 and are never touched
+// (those vectors are read ESZ bytes at a time)
+template <int IB, int ESZ, bool NT>
+__device__ __forceinline__ Dw<IB / 4> aligned_vec(const char* base, int64_t j, int64_t lo, int64_t hi) {
+    const int64_t o = j * IB;
+    Dw<IB / 4> r = dw_zero<IB / 4>();
+    if (o >= lo && o + IB <= hi) {
+        if constexpr (IB == 16) {
+            const v4u t = ld16<NT>(base + o);
+            r.d[0] = t.x; r.d[1] = t.y; r.d[2] = t.z; r.d[3] = t.w;
+        } else if constexpr (IB == 8) {
+            const v2u t = ld8<NT>(base + o);
+            r.d[0] = t.x; r.d[1] = t.y;
+        } else {
+            r.d[0] = ld4<NT>(base + o);
+        }
+    } else if (o < hi && o + IB > lo) {
+#pragma unroll
+        for (int e = 0; e < IB; e += ESZ) {
+            if (o + e >= lo && o + e + ESZ <= hi) {
+                if constexpr (ESZ == 4) r.d[e >> 2] = *(const uint32_t*)(base + o + e);
+                else if constexpr (ESZ == 2) r.d[e >> 2] |= (uint32_t)*(const uint16_t*)(base + o + e) << (8 * (e & 3));
+                else r.d[e >> 2] |= (uint32_t)*(const uint8_t*)(base + o + e) << (8 * (e & 3));
+            }
+        }
+    }
+    return r;
+}
+
+// the whole 4W-byte word w to the 4W-byte-aligned p
+template <int W, bool NT> __device__ __forceinline__ void store_full(uint8_t* p, const Dw<W>& w) {
+    if constexpr (W == 4) st16<NT>(p, v4u{w.d[0], w.d[1], w.d[2], w.d[3]});
+    else if constexpr (W == 2) st8<NT>(p, v2u{w.d[0], w.d[1]});
+    else st4<NT>(p, w.d[0]);
+}
+
+// bytes [lo, hi) of w (0 <= lo < hi <= 4W) to the 4W-byte-aligned word at p:
+// the whole word in one store, else in naturally aligned pieces of 4, 2 and
+// 1 bytes
+template <int W, bool NT>
+__device__ __forceinline__ void store_word(uint8_t* p, const Dw<W>& w, int lo, int hi) {
+    if (lo == 0 && hi == 4 * W) {
+        store_full<W, NT>(p, w);
+        return;
+    }
+#pragma unroll
+    for (int t = 0; t < W; ++t) {
+        const int l = lo - 4 * t > 0 ? lo - 4 * t : 0;
+        const int h = hi - 4 * t < 4 ? hi - 4 * t : 4;
+        if (l >= h) continue;
+        const uint32_t v = w.d[t];
+        uint8_t* q = p + 4 * t;
+        if (l == 0 && h == 4) {
+            *(uint32_t*)q = v;
+            continue;
+        }
+        int b = l;
+        if ((b & 1) && b < h) { q[b] = (uint8_t)(v >> (8 * b)); ++b; }
+        if (b + 2 <= h) { *(uint16_t*)(q + b) = (uint16_t)(v >> (8 * b)); b += 2; }
+        if (b < h) q[b] = (uint8_t)(v >> (8 * b));
+    }
+}
+
+// The shifted kernels carry amdgpu_num_sgpr(96): left alone the compiler
+// takes about 105 SGPRs for their uniform geometry, which allows 7 waves per
+// SIMD instead of 8, and the group cast ran 10 % slower.  A cap on waves per
+// SIMD instead made some of them spill VGPRs to scratch (the fp16 cast 50 %
+// slower).
+
+// Geometry of a shifted stream: input bytes [mx, xhi) from the IB-aligned xa,
+// output bytes [my, yhi) from the OB-aligned ya, nvec logical lane vectors
+// (the last one may be partial: its missing input reads as 0 and its output
+// past yhi is dropped).
+struct ShiftIO {
+    const char* xa;
+    int64_t xhi;
+    uint8_t* ya;
+    int64_t yhi;
+    int64_t nvec;
+    int mx, my;
+};
+
+template <int IB, int OB>
+__device__ __forceinline__ ShiftIO shift_io(const void* x, int64_t xbytes, void* y, int64_t ybytes, int64_t nvec) {
+    ShiftIO io;
+    io.mx = (int)((uintptr_t)x & (IB - 1));
+    io.my = (int)((uintptr_t)y & (OB - 1));
+    // pointer arithmetic, not a round trip through an integer: the compiler
+    // then still knows these address global memory and emits global (not
+    // flat) loads and stores
+    io.xa = (const char*)x - io.mx;
+    io.ya = (uint8_t*)y - io.my;
+    io.xhi = io.mx + xbytes;
+    io.yhi = io.my + ybytes;
+    io.nvec = nvec;
+    return io;
+}
+
+// the loads of one workgroup chunk (4 wave spans of K x 64 lane vectors)
+template <int IB, int K> struct ShiftLoads {
+    Dw<IB / 4> a[K];
+    Dw<IB / 4> e;   // lane 63: the aligned vector after the span
+};
+
+template <int IB, int ESZ, int K, bool NT>
+__device__ __forceinline__ void shift_load(ShiftLoads<IB, K>& L, const ShiftIO& io, int64_t c) {
+    const int lane = threadIdx.x & 63;
+    const int64_t v0 = (c * 4 + (threadIdx.x >> 6)) * (int64_t)(K * 64);
+#pragma unroll
+    for (int k = 0; k < K; ++k) L.a[k] = aligned_vec<IB, ESZ, NT>(io.xa, v0 + k * 64 + lane, io.mx, io.xhi);
+    L.e = dw_zero<IB / 4>();
+    if (io.mx != 0 && lane == 63) L.e = aligned_vec<IB, ESZ, NT>(io.xa, v0 + K * 64, io.mx, io.xhi);
+}
+
+// Convert and store one loaded chunk: op(in, v, valid, k) maps lane vector
+// v's input (IB bytes; sub-step k) to its output (OB bytes); it runs in every
+// lane, valid or not (a lane past the end sees zeros and must not read scale
+// arrays with v).  Lanes away from the span's ends and the output's end take
+// one full aligned store; the rest go through one rarely taken edge block.
+// XDW = (input address mod IB) / 4, fixed at compile time: the funnel's dword
+// selection is then static and only the next lane's dwords 0..XDW move.
+template <int IB, int OB, int K, bool NT, int XDW, typename Op>
+__device__ __forceinline__ void shift_convert(const ShiftLoads<IB, K>& L, const ShiftIO& io, int64_t c, Op&& op) {
+    static_assert(XDW >= 0 && XDW < IB / 4, "input dword offset");
+    constexpr int IW = IB / 4, OW = OB / 4;
+    const int lane = threadIdx.x & 63;
+    const int64_t v0 = (c * 4 + (threadIdx.x >> 6)) * (int64_t)(K * 64);
+    Dw<OW> carry = dw_zero<OW>();   // lane 63's output at the previous sub-step
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        Dw<IW> in = L.a[k];
+        if (io.mx != 0) {   // uniform
+            Dw<IW> nx = dw_zero<IW>();
+#pragma unroll
+            for (int d = 0; d <= XDW; ++d) {
+                const uint32_t sh = from_next_lane(L.a[k].d[d]);
+                uint32_t last = L.e.d[d];
+                if (k + 1 < K) last = lane_value(L.a[(k + 1) % K].d[d], 0);   // k is a constant here
+                nx.d[d] = lane == 63 ? last : sh;
+            }
+            in = funnel_static<IW, XDW>(L.a[k], nx, io.mx & 3);
+        }
+        const int64_t v = v0 + k * 64 + lane;
+        const bool valid = v < io.nvec;
+        const Dw<OW> out = op(in, v, valid, k);
+        const int64_t ob = v * OB;   // the aligned output word at ya + ob ends inside this lane's output
+        if (io.my == 0) {
+            if (valid) {
+                const int64_t hi = io.yhi - ob;
+                if (hi >= OB) store_full<OW, NT>(io.ya + ob, out);
+                else store_word<OW, NT>(io.ya + ob, out, 0, (int)hi);
+            }
+            continue;
+        }
+        Dw<OW> pv;
+#pragma unroll
+        for (int d = 0; d < OW; ++d) {
+            const uint32_t sh = from_prev_lane(out.d[d]);
+            pv.d[d] = lane == 0 ? carry.d[d] : sh;
+        }
+        if (valid) {
+            const Dw<OW> w = funnel<OW>(pv, out, OB - io.my);
+            const int64_t hi = io.yhi - ob;
+            const bool head = lane == 0 && k == 0;                           // no previous lane's bytes here
+            const bool tail = (lane == 63 && k == K - 1) || v == io.nvec - 1;   // own trailing bytes too
+            if (!head && !tail && hi >= OB) {
+                store_full<OW, NT>(io.ya + ob, w);
+            } else {
+                const int lo = head ? io.my : 0;
+                if (lo < hi) store_word<OW, NT>(io.ya + ob, w, lo, hi < OB ? (int)hi : OB);
+                const int64_t hi2 = hi - OB;
+                if (tail && hi2 > 0) {
+                    const Dw<OW> t = funnel<OW>(out, dw_zero<OW>(), OB - io.my);
+                    store_word<OW, NT>(io.ya + ob + OB, t, 0, hi2 < io.my ? (int)hi2 : io.my);
+                }
+            }
+        }
+        if (k + 1 < K) {
+#pragma unroll
+            for (int d = 0; d < OW; ++d) carry.d[d] = lane_value(out.d[d], 63);
+        }
+    }
 }
 
 // ===========================================================================
@@ -427,173 +711,41 @@ k_group128_pair(const void* __restrict__ x, uint8_t* __restrict__ q, float* __re
     }
 }
 
-// Shifted path, for x aligned only to its element size and q to nothing (a
-// view that starts a few elements into a buffer).  The lanes keep
-// k_group128's shape (LPG lanes x VE elements per group, one 16-byte load and
-// one VE-byte store each) and every global access stays aligned.  Each wave
-// takes a contiguous span of K x 64 lane vectors (K sub-steps of 64):
-//  - load side: lane t loads the 16-byte-aligned vector holding the start of
-//    its VE elements and takes the next lane's leading dwords by a whole-wave
-//    DPP shift; lane 63 takes them from lane 0's vector of the next sub-step
-//    (a readlane), and at the span's last sub-step from one extra load.  A
-//    byte shift (v_alignbyte) then forms the lane's elements.
-//  - store side: lane t writes the VE-aligned word that ends inside its codes,
-//    the previous lane's trailing bytes (DPP shift; for lane 0, lane 63's codes
-//    of the previous sub-step) then its own leading bytes.  Only the span's
-//    first lane writes just its own bytes, and only the span's last lane (or
-//    the lane holding the tensor's last vector) writes its trailing bytes on
-//    its own, in the widest aligned pieces that fit.
-// The two 16-byte vectors that straddle either end of x are read element by
-// element over the bytes x holds, so nothing outside x or q is touched.
-// XDW = (x mod 16) / 4 is a template argument so that the dword selection is
-// fixed at compile time; the byte shift within a dword (x mod 4: 0, or 2 for
-// the 16-bit types) and q's offset from a VE-byte boundary are runtime values,
-// uniform across the grid.
-
-// x's 16-byte-aligned vector j (at xa + 16 j), with the bytes outside
-// [lo, hi) (offsets from xa) read as zero and never touched.  Lanes beyond the
-// tensor take all zeros.
-template <int ESZ, bool NT>
-__device__ __forceinline__ v4u aligned_vec16(const char* xa, int64_t j, int64_t lo, int64_t hi) {
-    const int64_t o = j * 16;
-    if (o >= lo && o + 16 <= hi) return ld16<NT>(xa + o);
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
-    if (o < hi && o + 16 > lo) {
-#pragma unroll
-        for (int e = 0; e < 16; e += ESZ) {
-            if (o + e >= lo && o + e + ESZ <= hi) {
-                if constexpr (ESZ == 4) w[e >> 2] = *(const uint32_t*)(xa + o + e);
-                else w[e >> 2] |= (uint32_t)*(const uint16_t*)(xa + o + e) << (8 * (e & 3));
-            }
-        }
-    }
-    return v4u{w[0], w[1], w[2], w[3]};
-}
-
-// bytes [lo, hi) of w (little-endian) to the W-byte-aligned word at p, in
-// naturally aligned pieces of 4, 2 and 1 bytes
-template <typename W>
-__device__ __forceinline__ void store_bytes(uint8_t* p, W w, int lo, int hi) {
-    for (int b = lo; b < hi;) {
-        if ((b & 3) == 0 && b + 4 <= hi) {
-            *(uint32_t*)(p + b) = (uint32_t)(w >> (8 * b));
-            b += 4;
-        } else if ((b & 1) == 0 && b + 2 <= hi) {
-            *(uint16_t*)(p + b) = (uint16_t)(w >> (8 * b));
-            b += 2;
-        } else {
-            p[b] = (uint8_t)(w >> (8 * b));
-            b += 1;
-        }
-    }
-}
-
-// whole-wave DPP lane shifts (bound_ctrl off: the lane with no source keeps 0)
-__device__ __forceinline__ uint32_t from_next_lane(uint32_t v) {   // lane t <- lane t + 1 (wave_shl:1)
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x130, 0xF, 0xF, false);
-}
-__device__ __forceinline__ uint32_t from_prev_lane(uint32_t v) {   // lane t <- lane t - 1 (wave_shr:1)
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x138, 0xF, 0xF, false);
-}
-__device__ __forceinline__ uint32_t lane_value(uint32_t v, int lane) {
-    return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
-}
-
+// Shifted path, for x not 16-byte aligned or q not 4-byte aligned (a view
+// that starts a few elements into its buffer): k_group128's lanes (LPG lanes
+// x VE elements per group) on the shifted stream, so every global access but
+// a few at the edges of each wave span stays an aligned vector access.  The
+// groups never straddle lane vectors and there are whole groups only, so no
+// vector is partial; the group max runs over full groups of lanes.
+// XDW: (x mod 16) / 4.
 template <int DT, int FMT, int K, int XDW>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_num_sgpr(96)))
 k_group128_shift(const void* __restrict__ x, uint8_t* __restrict__ q, float* __restrict__ sinv_out, int64_t groups) {
     constexpr int VE = LaneVE<DT>::value;
     constexpr int ESZ = ESize<DT>::value;
     constexpr int LPG = 128 / VE;
-    constexpr int GPW = 64 / LPG;                   // groups per wave sub-step
-    constexpr int CH = K * 4 * GPW;                 // groups per workgroup chunk
-    using Word = typename std::conditional<VE == 8, uint64_t, uint32_t>::type;
-    const int mx = (int)((uintptr_t)x & 15);        // 4 * XDW + xsb
-    const int xsb = mx & 3;
-    const int mq = (int)((uintptr_t)q & (VE - 1));
-    const char* xa = (const char*)x - mx;            // 16-byte aligned
-    uint8_t* qa = q - mq;                            // VE-byte aligned
-    const int64_t nvec = groups * LPG;               // x's lane vectors (16 bytes each)
-    const int64_t xhi = mx + nvec * 16;              // x's bytes are [mx, xhi) from xa
-    const int lane = threadIdx.x & 63;
-    const int lig = lane % LPG;
-    const int64_t nchunks = (groups + CH - 1) / CH;
+    constexpr int OB = VE;                          // code bytes per lane vector
+    const ShiftIO io = shift_io<16, OB>(x, groups * 128 * ESZ, q, groups * 128, groups * LPG);
+    const int64_t nchunks = (io.nvec + K * 256 - 1) / (K * 256);
     for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
-        const int64_t g0 = c * CH + (int64_t)(threadIdx.x >> 6) * (K * GPW);   // the wave's first group
-        const int64_t v0 = g0 * LPG;                                             // and first lane vector
-        v4u a[K];
-#pragma unroll
-        for (int k = 0; k < K; ++k) a[k] = aligned_vec16<ESZ, true>(xa, v0 + k * 64 + lane, mx, xhi);
-        v4u e = v4u{0u, 0u, 0u, 0u};
-        if (mx != 0 && lane == 63) e = aligned_vec16<ESZ, true>(xa, v0 + K * 64, mx, xhi);
-        uint32_t plo = 0u, phi = 0u;   // lane 63's codes at the previous sub-step
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-            // every lane is active here
-            uint32_t s[8] = {a[k].x, a[k].y, a[k].z, a[k].w, 0u, 0u, 0u, 0u};
-            if (mx != 0) {   // uniform
-#pragma unroll
-                for (int d = 0; d <= XDW; ++d) {
-                    const uint32_t nx = from_next_lane(s[d]);   // straight-line, every lane active
-                    uint32_t last = e[d];
-                    if (k + 1 < K) last = lane_value(a[(k + 1) % K][d], 0);   // k is a constant here
-                    s[4 + d] = lane == 63 ? last : nx;
-                }
-            }
-            HpVec<DT> v;
-            v.r = v4u{__builtin_amdgcn_alignbyte(s[XDW + 1], s[XDW + 0], xsb),
-                      __builtin_amdgcn_alignbyte(s[XDW + 2], s[XDW + 1], xsb),
-                      __builtin_amdgcn_alignbyte(s[XDW + 3], s[XDW + 2], xsb),
-                      __builtin_amdgcn_alignbyte(s[XDW + 4], s[XDW + 3], xsb)};
-            const int64_t g = g0 + k * GPW + lane / LPG;
-            Word cw = 0;
-            if (g < groups) {  // uniform within the LPG lanes of a group; valid lanes are a prefix
-                const uint32_t amax = max_lanes<LPG>(v.absmax_bits());
+        ShiftLoads<16, K> L;
+        shift_load<16, ESZ, K, true>(L, io, c);
+        shift_convert<16, OB, K, true, XDW>(L, io, c, [&](const Dw<4>& in, int64_t v, bool valid, int) {
+            HpVec<DT> h;
+            h.r = v4u{in.d[0], in.d[1], in.d[2], in.d[3]};
+            Dw<OB / 4> o = dw_zero<OB / 4>();
+            if (valid) {   // uniform within the LPG lanes of a group
+                const uint32_t amax = max_lanes<LPG>(h.absmax_bits());
                 float scale, sinv;
                 group_scale<FMT>(amax, scale, sinv);
                 float f[VE];
-                v.widen(f);
-                if constexpr (VE == 8) {
-                    cw = (uint64_t)enc4<FMT>(f[0] * scale, f[1] * scale, f[2] * scale, f[3] * scale) |
-                         ((uint64_t)enc4<FMT>(f[4] * scale, f[5] * scale, f[6] * scale, f[7] * scale) << 32);
-                } else {
-                    cw = enc4<FMT>(f[0] * scale, f[1] * scale, f[2] * scale, f[3] * scale);
-                }
-                const int64_t vi = v0 + k * 64 + lane;  // this lane's vector; its codes are q[VE vi, VE vi + VE)
-                uint8_t* wq = qa + vi * VE;             // the aligned word holding the first of them
-                if (mq == 0) {
-                    if constexpr (VE == 8) st8<true>(wq, v2u{(uint32_t)cw, (uint32_t)(cw >> 32)});
-                    else st4<true>(wq, cw);
-                } else {
-                    // the previous lane's codes (lane t - 1 is valid whenever lane t
-                    // is).  The DPP shifts run in straight-line code, outside any
-                    // condition on the lane: a shift executed under a mask that
-                    // disables its source lane reads 0 instead of that lane.
-                    Word pw;
-                    if constexpr (VE == 8) {
-                        const uint32_t lo = from_prev_lane((uint32_t)cw), hi = from_prev_lane((uint32_t)(cw >> 32));
-                        pw = lane == 0 ? ((uint64_t)plo | ((uint64_t)phi << 32)) : ((uint64_t)lo | ((uint64_t)hi << 32));
-                    } else {
-                        const uint32_t lo = from_prev_lane(cw);
-                        pw = lane == 0 ? plo : lo;
-                    }
-                    const Word w = (Word)(cw << (8 * mq)) | (Word)(pw >> (8 * (VE - mq)));
-                    if (lane != 0 || k > 0) {
-                        if constexpr (VE == 8) st8<true>(wq, v2u{(uint32_t)w, (uint32_t)(w >> 32)});
-                        else st4<true>(wq, w);
-                    } else {
-                        store_bytes<Word>(wq, w, mq, VE);
-                    }
-                    if ((lane == 63 && k == K - 1) || vi == nvec - 1)
-                        store_bytes<Word>(wq + VE, (Word)(cw >> (8 * (VE - mq))), 0, mq);
-                }
-                if (lig == 0) sinv_out[g] = sinv;
+                h.widen(f);
+                o.d[0] = enc4<FMT>(f[0] * scale, f[1] * scale, f[2] * scale, f[3] * scale);
+                if constexpr (VE == 8) o.d[1] = enc4<FMT>(f[4] * scale, f[5] * scale, f[6] * scale, f[7] * scale);
+                if ((threadIdx.x & (LPG - 1)) == 0) sinv_out[(uint64_t)v / LPG] = sinv;
             }
-            if (mq != 0 && k + 1 < K) {
-                plo = lane_value((uint32_t)cw, 63);
-                if constexpr (VE == 8) phi = lane_value((uint32_t)((uint64_t)cw >> 32), 63);
-            }
-        }
+            return o;
+        });
     }
 }
 
@@ -607,25 +759,6 @@ k_group128_shift(const void* __restrict__ x, uint8_t* __restrict__ q, float* __r
 // workgroup's result into slot (workgroup % nslots); slot i is the word at
 // i * kAmaxSlotStride, one slot per 128-byte line.  Device-scope atomics
 // serialise per cache line, so slots sharing a line gain nothing.
-
-// clear the amax slots (a kernel rather than hipMemsetAsync, so the call
-// can be captured into a HIP graph)
-__global__ void k_fill_slots(uint32_t* p, int nslots, uint32_t v) {
-    if ((int)threadIdx.x < nslots) p[threadIdx.x * kAmaxSlotStride] = v;
-}
-
-// where(amax > 0, amax, 1) in place (a NaN amax also becomes 1), on one word
-__global__ void k_guard_amax(uint32_t* p) {
-    if (threadIdx.x == 0) {
-        const float v = __uint_as_float(p[0]);
-        p[0] = __float_as_uint(v > 0.0f ? v : 1.0f);
-    }
-}
-
-__global__ void k_fill_f32(float* p, int64_t n, float v) {
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-        p[i] = v;
-}
 
 // VEC (x 16-B aligned): chunks of K sub-steps x 256 lane vectors per
 // workgroup trip; the n % VE tail element-wise by workgroup 0.
@@ -663,6 +796,41 @@ k_amax(const void* __restrict__ x, int64_t n, uint32_t* __restrict__ amax_bits, 
     } else {
         for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
             m = umax(m, absbits1<DT>(x, i));
+    }
+    m = block_max256(m, lds);
+    if constexpr (PART) {
+        if (threadIdx.x == 0) amax_bits[blockIdx.x] = m;
+    } else {
+        if (threadIdx.x == 0 && m != 0) atomicMax(amax_bits + (blockIdx.x % nslots) * kAmaxSlotStride, m);
+    }
+}
+
+// The amax of an x that is aligned to its element size only: the aligned
+// 16-byte vectors that cover it, the two that straddle its ends read element
+// by element over the bytes x holds (zeros elsewhere, which a max of |x| bit
+// patterns ignores).  Chunks of K sub-steps x 256 aligned vectors per
+// workgroup trip; stage 2 as k_amax.
+template <int DT, int K, bool NT, bool PART = false>
+__global__ void __launch_bounds__(256)
+k_amax_shift(const void* __restrict__ x, int64_t n, uint32_t* __restrict__ amax_bits, int nslots) {
+    __shared__ uint32_t lds[4];
+    constexpr int ESZ = ESize<DT>::value;
+    const int mx = (int)((uintptr_t)x & 15);
+    const char* xa = (const char*)x - mx;   // pointer arithmetic keeps the global address space
+    const int64_t xhi = mx + n * ESZ;
+    const int64_t nal = (xhi + 15) / 16;
+    const int64_t nchunks = (nal + K * 256 - 1) / (K * 256);
+    uint32_t m = 0;
+    for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+        Dw<4> v[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) v[k] = aligned_vec<16, ESZ, NT>(xa, (c * K + k) * 256 + threadIdx.x, mx, xhi);
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            HpVec<DT> h;
+            h.r = v4u{v[k].d[0], v[k].d[1], v[k].d[2], v[k].d[3]};
+            m = umax(m, h.absmax_bits());
+        }
     }
     m = block_max256(m, lds);
     if constexpr (PART) {
@@ -851,6 +1019,96 @@ k_pipeline_cast(const void* __restrict__ x, int64_t n, const uint32_t* __restric
         pipeline_cast_rest<DT, kE5M2, VEC, K, NT>(v, x, n, ab, q, sinv_out, fmt_out);
     else
         pipeline_cast_rest<DT, kE4M3, VEC, K, NT>(v, x, n, ab, q, sinv_out, fmt_out);
+}
+
+// The same casts for x aligned to its element size only or q to nothing:
+// the shifted stream (16-byte input vectors, VE code bytes out).  The casts'
+// arithmetic is the vector path's, lane vector by lane vector.
+template <int DT, int FMT, int K, bool NT, int XDW, bool SAT>
+__device__ __forceinline__ void cast_shift_chunks(ShiftLoads<16, K>& L, const ShiftIO& io, float scale) {
+    constexpr int VE = LaneVE<DT>::value;
+    const int64_t nchunks = (io.nvec + K * 256 - 1) / (K * 256);
+    for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+        if (c != (int64_t)blockIdx.x) shift_load<16, ESize<DT>::value, K, NT>(L, io, c);
+        shift_convert<16, VE, K, NT, XDW>(L, io, c, [&](const Dw<4>& in, int64_t, bool, int) {
+            HpVec<DT> h;
+            h.r = v4u{in.d[0], in.d[1], in.d[2], in.d[3]};
+            float f[VE];
+            h.widen(f);
+            float p[VE];
+#pragma unroll
+            for (int e = 0; e < VE; ++e) {
+                p[e] = f[e] * scale;
+                if constexpr (SAT) p[e] = sat<FMT>(p[e]);
+            }
+            Dw<VE / 4> o;
+            o.d[0] = enc4<FMT>(p[0], p[1], p[2], p[3]);
+            if constexpr (VE == 8) o.d[1] = enc4<FMT>(p[4], p[5], p[6], p[7]);
+            return o;
+        });
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ ShiftIO cast_shift_io(const void* x, int64_t n, uint8_t* q) {
+    constexpr int VE = LaneVE<DT>::value;
+    return shift_io<16, VE>(x, n * ESize<DT>::value, q, n, (n + VE - 1) / VE);
+}
+
+template <int DT, int FMT, int K, bool NT, int XDW>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_num_sgpr(96)))
+k_tensor_cast_shift(const void* __restrict__ x, int64_t n, const uint32_t* __restrict__ partial, int np,
+                    int pstride, uint8_t* __restrict__ q, float* __restrict__ sinv_out) {
+    __shared__ uint32_t lds[4];
+    const ShiftIO io = cast_shift_io<DT>(x, n, q);
+    ShiftLoads<16, K> L;
+    shift_load<16, ESize<DT>::value, K, NT>(L, io, blockIdx.x);   // its latency hides behind the fold
+    const uint32_t ab = fold_partials(partial, np, pstride, lds);
+    float scale, sinv;
+    tensor_scale<FMT>(ab, scale, sinv);
+    if (blockIdx.x == 0 && threadIdx.x == 0) sinv_out[0] = sinv;
+    if (needs_saturation(ab, scale)) cast_shift_chunks<DT, FMT, K, NT, XDW, true>(L, io, scale);   // uniform
+    else cast_shift_chunks<DT, FMT, K, NT, XDW, false>(L, io, scale);
+}
+
+template <int DT, int FMT, int K, bool NT, int XDW>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_num_sgpr(96)))
+k_cast_given_amax_shift(const void* __restrict__ x, int64_t n, const float* __restrict__ amax,
+                        uint8_t* __restrict__ q, float* __restrict__ scale_out) {
+    const float scale = Fp8Fmt<FMT>::max / amax[0];
+    if (blockIdx.x == 0 && threadIdx.x == 0) scale_out[0] = scale;
+    const ShiftIO io = cast_shift_io<DT>(x, n, q);
+    ShiftLoads<16, K> L;
+    shift_load<16, ESize<DT>::value, K, NT>(L, io, blockIdx.x);
+    cast_shift_chunks<DT, FMT, K, NT, XDW, true>(L, io, scale);
+}
+
+template <int DT, int FMT, int K, bool NT, int XDW>
+__device__ __forceinline__ void pipeline_cast_shift_rest(ShiftLoads<16, K>& L, const ShiftIO& io, uint32_t ab,
+                                                         float* __restrict__ sinv_out, int32_t* __restrict__ fmt_out) {
+    const float amax = __uint_as_float(ab);
+    const float scale = (amax == 0.0f) ? 1.0f : Fp8Fmt<FMT>::max / amax;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        sinv_out[0] = 1.0f / scale;
+        fmt_out[0] = FMT;
+    }
+    if (needs_saturation(ab, scale)) cast_shift_chunks<DT, FMT, K, NT, XDW, true>(L, io, scale);
+    else cast_shift_chunks<DT, FMT, K, NT, XDW, false>(L, io, scale);
+}
+
+template <int DT, int K, bool NT, int XDW>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_num_sgpr(96)))
+k_pipeline_cast_shift(const void* __restrict__ x, int64_t n, const uint32_t* __restrict__ partial, int np,
+                      uint8_t* __restrict__ q, float* __restrict__ sinv_out, int32_t* __restrict__ fmt_out) {
+    __shared__ uint32_t lds[4];
+    const ShiftIO io = cast_shift_io<DT>(x, n, q);
+    ShiftLoads<16, K> L;
+    shift_load<16, ESize<DT>::value, K, NT>(L, io, blockIdx.x);
+    const uint32_t ab = fold_partials(partial, np, 1, lds);
+    if (__uint_as_float(ab) > Fp8Fmt<kE4M3>::max)
+        pipeline_cast_shift_rest<DT, kE5M2, K, NT, XDW>(L, io, ab, sinv_out, fmt_out);
+    else
+        pipeline_cast_shift_rest<DT, kE4M3, K, NT, XDW>(L, io, ab, sinv_out, fmt_out);
 }
 
 // ===========================================================================
@@ -1115,6 +1373,61 @@ k_dequant_flat(const uint8_t* __restrict__ q, int64_t n, const float* __restrict
     dequant_flat_body<FMT, YDT, MODE, VEC, K, NT>(q, n, sinv, y, blockIdx.x, gridDim.x, blockIdx.x == 0);
 }
 
+// The flat dequants for q or y aligned to their element size only: the
+// shifted stream (VE code bytes in, 16-byte output vectors), with the vector
+// path's arithmetic lane vector by lane vector.
+template <int FMT, int YDT, int MODE, int K, bool NT, int XDW>
+__device__ __forceinline__ void dequant_shift_body(const uint8_t* __restrict__ q, int64_t n,
+                                                   const float* __restrict__ sinv, void* __restrict__ y) {
+    constexpr int VE = LaneVE<YDT>::value;
+    const ShiftIO io = shift_io<VE, 16>(q, n, y, n * ESize<YDT>::value, (n + VE - 1) / VE);
+    const int64_t nchunks = (io.nvec + K * 256 - 1) / (K * 256);
+    const float s0 = (MODE != 2) ? sinv[0] : 0.0f;
+    for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+        ShiftLoads<VE, K> L;
+        shift_load<VE, 1, K, NT>(L, io, c);
+        float sk[K];   // per-group scales, loaded beside the codes
+        if constexpr (MODE == 2) {
+            const int64_t v0 = (c * 4 + (threadIdx.x >> 6)) * (int64_t)(K * 64) + (threadIdx.x & 63);
+#pragma unroll
+            for (int k = 0; k < K; ++k) sk[k] = (v0 + k * 64 < io.nvec) ? sinv[((v0 + k * 64) * VE) >> 7] : 0.0f;
+        }
+        shift_convert<VE, 16, K, NT, XDW>(L, io, c, [&](const Dw<VE / 4>& in, int64_t, bool, int k) {
+            Fp8Vec<FMT, VE, NT> w;
+#pragma unroll
+            for (int d = 0; d < VE / 4; ++d) w.w[d] = in.d[d];
+            float p[VE];
+            if constexpr (MODE == 3) {
+                w.decode_scaled(1.0f, p);
+#pragma unroll
+                for (int e = 0; e < VE; ++e) p[e] = p[e] / s0;
+            } else {
+                w.decode_scaled((MODE == 0) ? s0 : sk[k], p);
+            }
+            const v4u o = pack_out16<YDT>(p);
+            return Dw<4>{{o.x, o.y, o.z, o.w}};
+        });
+    }
+}
+
+template <int FMT, int YDT, int MODE, int K, bool NT, int XDW>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_num_sgpr(96)))
+k_dequant_flat_shift(const uint8_t* __restrict__ q, int64_t n, const float* __restrict__ sinv, void* __restrict__ y) {
+    dequant_shift_body<FMT, YDT, MODE, K, NT, XDW>(q, n, sinv, y);
+}
+
+template <int YDT, int K, bool NT, int XDW>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_num_sgpr(96)))
+k_dequant_pipeline_shift(const uint8_t* __restrict__ q, int64_t n, const float* __restrict__ sinv,
+                         const int32_t* __restrict__ fmt, void* __restrict__ y) {
+    const int32_t f = fmt[0];
+    if (f == kE4M3) dequant_shift_body<kE4M3, YDT, 0, K, NT, XDW>(q, n, sinv, y);
+    else if (f == kE5M2) dequant_shift_body<kE5M2, YDT, 0, K, NT, XDW>(q, n, sinv, y);
+    else
+        for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+            store1<YDT>(y, i, __builtin_nanf(""));
+}
+
 // Dequant of W packed slots (ColossalAI fp8.py, all_gather_fp8_lagacy and
 // all_gather_fp8_ring, receive side): slot w starts at slots + w * (4 + n)
 // with its binary32 scale_inv in bytes 0..3 and n codes after it; output w
@@ -1225,6 +1538,35 @@ k_dequant_rows_flat(const uint8_t* __restrict__ q, int64_t nvec, const float* __
                 store_out16<YDT, NT>(y, vi * VE, p);
             }
         }
+    }
+}
+
+// The same for q or y aligned to their element size only: the shifted
+// stream, each lane's row by the same division (cols % VE == 0, so a lane
+// vector never straddles two rows).
+template <int FMT, int YDT, int K, bool NT, int XDW>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_num_sgpr(96)))
+k_dequant_rows_shift(const uint8_t* __restrict__ q, int64_t nvec, const float* __restrict__ sinv,
+                     void* __restrict__ y, DivU32 dvpr) {
+    constexpr int VE = LaneVE<YDT>::value;
+    const ShiftIO io = shift_io<VE, 16>(q, nvec * VE, y, nvec * VE * ESize<YDT>::value, nvec);
+    const int64_t nchunks = (nvec + K * 256 - 1) / (K * 256);
+    for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+        ShiftLoads<VE, K> L;
+        shift_load<VE, 1, K, NT>(L, io, c);
+        float sk[K];   // row scales, loaded beside the codes
+        const int64_t v0 = (c * 4 + (threadIdx.x >> 6)) * (int64_t)(K * 64) + (threadIdx.x & 63);
+#pragma unroll
+        for (int k = 0; k < K; ++k) sk[k] = (v0 + k * 64 < nvec) ? sinv[div_u32((uint32_t)(v0 + k * 64), dvpr)] : 0.0f;
+        shift_convert<VE, 16, K, NT, XDW>(L, io, c, [&](const Dw<VE / 4>& in, int64_t, bool, int k) {
+            Fp8Vec<FMT, VE, NT> w;
+#pragma unroll
+            for (int d = 0; d < VE / 4; ++d) w.w[d] = in.d[d];
+            float p[VE];
+            w.decode_scaled(sk[k], p);
+            const v4u o = pack_out16<YDT>(p);
+            return Dw<4>{{o.x, o.y, o.z, o.w}};
+        });
     }
 }
 

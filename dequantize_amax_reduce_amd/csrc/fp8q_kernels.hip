@@ -25,81 +25,28 @@
 #include <type_traits>
 
 #include "fp8q_device.h"
+#include "fp8q_host.h"
 
 namespace fp8q {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int64_t kGridCap = 1 << 20;   // grid-stride beyond this many workgroups
-constexpr int64_t kAmaxGrid = kAmaxPartials;  // amax-pass workgroups (and partials)
-constexpr int64_t kSumAmaxGrid = 8192;  // the reduce step's sum pass when it also folds the amax
-
-constexpr int kGroupK = 2;        // sub-steps per group-cast chunk
-constexpr int kFlatK = 2;         // sub-steps per flat chunk outside pick_flat_k's window
-constexpr int kAmaxK = 2;         // sub-steps per amax chunk
-constexpr int kBlockK = 2;        // sub-steps per block-dequant chunk
-constexpr int kBlockRows = 1;     // rows per workgroup in the row-strip fallback
-constexpr int kBlockU = 2;        // lane vectors per row per thread in flight there
-constexpr int kSumKV = 2;         // lane vectors per thread in the reduce-step sum
-constexpr bool kNT = true;        // non-temporal loads/stores for streaming data
-
-inline bool al(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
-
-inline unsigned grid(int64_t units) {
-    int64_t b = units < 1 ? 1 : units;
-    if (b > kGridCap) b = kGridCap;
-    return (unsigned)b;
+// clear the amax slots (a kernel rather than hipMemsetAsync, so the call
+// can be captured into a HIP graph)
+__global__ void k_fill_slots(uint32_t* p, int nslots, uint32_t v) {
+    if ((int)threadIdx.x < nslots) p[threadIdx.x * kAmaxSlotStride] = v;
 }
 
-// invariant-divisor constants for dividing a 32-bit lane-vector index by d >= 1
-inline DivU32 make_div(uint32_t d) {
-    int l = 0;
-    while ((uint64_t(1) << l) < d) ++l;
-    return DivU32{(uint32_t)((((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d) + 1), l};
-}
-
-template <int K> using KC = std::integral_constant<int, K>;
-
-// Sub-steps per chunk (K) of a flat kernel over u1 = ceil(nvec / 256) chunks
-// of one sub-step, with a grid covering the tensor.  K = 2 in general; a
-// tensor whose K = 2 grid would take two to four dispatch rounds of
-// workgroups (256 CUs x 8 resident workgroups = 2048 per round) instead gets
-// the K that brings the grid to about one round.  Measured on the flat
-// dequants, e4m3fn -> bf16 / fp32 from 2^20 to 2^27 elements: bf16 2^24
-// 10.0 us with K = 4 against 11.4 us with K = 2; fp32 2^23 8.3-8.5 against
-// 9.9 us; at 2^25 elements and above K = 2 is fastest again (bf16 2^27: 66.6
-// us against 71.1 with K = 4), and below 2^23 the choice makes no difference.
-inline int pick_flat_k(int64_t u1) {
-    if (u1 > 4096 && u1 <= 8192) return 4;
-    if (u1 > 8192 && u1 <= 16384) return 8;
-    return 2;
-}
-
-// launch(KC<K>{}, grid) for the K pick_flat_k chooses over nvec lane vectors
-template <typename L> void launch_k(int64_t nvec, L&& launch) {
-    const int64_t u1 = (nvec + 255) / 256;
-    const int K = pick_flat_k(u1);
-    if (K == 8) launch(KC<8>{}, grid((u1 + 7) / 8));
-    else if (K == 4) launch(KC<4>{}, grid((u1 + 3) / 4));
-    else launch(KC<2>{}, grid((u1 + 1) / 2));
-}
-
-template <template <int, int> class F, typename... A>
-void dispatch_dt_fmt(int dt, int fmt, A... a) {
-    if (dt == kF32) { if (fmt == kE4M3) F<kF32, kE4M3>::run(a...); else F<kF32, kE5M2>::run(a...); }
-    else if (dt == kBF16) { if (fmt == kE4M3) F<kBF16, kE4M3>::run(a...); else F<kBF16, kE5M2>::run(a...); }
-    else { if (fmt == kE4M3) F<kF16, kE4M3>::run(a...); else F<kF16, kE5M2>::run(a...); }
-}
-
-template <template <int, int> class F, typename... A>
-void dispatch_fmt_ydt(int fmt, int ydt, A... a) {
-    if (fmt == kE4M3) {
-        if (ydt == kF32) F<kE4M3, kF32>::run(a...); else if (ydt == kBF16) F<kE4M3, kBF16>::run(a...);
-        else F<kE4M3, kF16>::run(a...);
-    } else {
-        if (ydt == kF32) F<kE5M2, kF32>::run(a...); else if (ydt == kBF16) F<kE5M2, kBF16>::run(a...);
-        else F<kE5M2, kF16>::run(a...);
+// where(amax > 0, amax, 1) in place (a NaN amax also becomes 1), on one word
+__global__ void k_guard_amax(uint32_t* p) {
+    if (threadIdx.x == 0) {
+        const float v = __uint_as_float(p[0]);
+        p[0] = __float_as_uint(v > 0.0f ? v : 1.0f);
     }
+}
+
+__global__ void k_fill_f32(float* p, int64_t n, float v) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = v;
 }
 
 
@@ -111,14 +58,7 @@ template <int DT, int FMT> struct RunGroup128 {
         if (al(x, 16) && al(q, 4)) {
             k_group128<DT, FMT, kGroupK, kNT><<<nb, kThreads, 0, st>>>(x, q, sinv, groups);
         } else {
-            // x is aligned to its element size (checked at the boundary), so
-            // x mod 16 is a whole number of elements
-            switch (((uintptr_t)x & 15) >> 2) {
-                case 0: k_group128_shift<DT, FMT, kGroupK, 0><<<nb, kThreads, 0, st>>>(x, q, sinv, groups); break;
-                case 1: k_group128_shift<DT, FMT, kGroupK, 1><<<nb, kThreads, 0, st>>>(x, q, sinv, groups); break;
-                case 2: k_group128_shift<DT, FMT, kGroupK, 2><<<nb, kThreads, 0, st>>>(x, q, sinv, groups); break;
-                default: k_group128_shift<DT, FMT, kGroupK, 3><<<nb, kThreads, 0, st>>>(x, q, sinv, groups); break;
-            }
+            launch_group128_shift(x, DT, groups, FMT, q, sinv, st);
         }
     }
 };
@@ -156,9 +96,8 @@ template <int DT, int FMT> struct RunTensorCast {
                 k_tensor_cast<DT, FMT, true, decltype(K)::value, kNT><<<nb, kThreads, 0, st>>>(x, n, partial, np,
                                                                                                pstride, q, sinv);
             });
-        } else {
-            k_tensor_cast<DT, FMT, false, kFlatK, kNT><<<grid((n + 255) / 256), kThreads, 0, st>>>(x, n, partial, np,
-                                                                                                  pstride, q, sinv);
+        } else {   // the shifted stream, with the amax pass's sub-steps per chunk (amax_plan)
+            launch_tensor_cast_shift(x, DT, n, FMT, partial, np, pstride, q, sinv, st);
         }
     }
 };
@@ -172,8 +111,7 @@ template <int DT, int FMT> struct RunCastGivenAmax {
                                                                                                    scale_out);
             });
         } else {
-            k_cast_given_amax<DT, FMT, false, kFlatK, kNT><<<grid((n + 255) / 256), kThreads, 0, st>>>(x, n, amax, q,
-                                                                                                       scale_out);
+            launch_cast_given_amax_shift(x, DT, n, FMT, amax, q, scale_out, st);
         }
     }
 };
@@ -226,8 +164,10 @@ template <int DT> void run_amax(const void* x, int64_t n, uint32_t* word, hipStr
         k_amax<DT, true, kAmaxK, kNT><<<(unsigned)std::min(std::max<int64_t>(chunks, 1), cap), kThreads, 0, st>>>(
             x, n, word, 1);
     } else {
-        k_amax<DT, false, kAmaxK, false><<<(unsigned)std::min((n + 255) / 256, cap), kThreads, 0, st>>>(x, n, word,
-                                                                                                       1);
+        const int64_t mx = (int64_t)((uintptr_t)x & 15);
+        const int64_t chunks = ((mx + n * ESize<DT>::value + 15) / 16 + kAmaxK * 256 - 1) / (kAmaxK * 256);
+        k_amax_shift<DT, kAmaxK, kNT><<<(unsigned)std::min(std::max<int64_t>(chunks, 1), cap), kThreads, 0, st>>>(
+            x, n, word, 1);
     }
 }
 
@@ -241,27 +181,40 @@ template <int DT> void run_amax(const void* x, int64_t n, uint32_t* word, hipStr
 // [4096, 4096] cast takes 16.4 us against 20.8 us, fp32 28.5 against 31.9.
 // The vector amax pass takes the sub-steps per chunk its cast pass will take
 // (pick_flat_k, see RunTensorCast); the element-wise one takes kAmaxK.
-template <int DT> int amax_partials_grid(const void* x, int64_t n) {
+// The amax pass's sub-steps per chunk K (the cast pass's, so that chunk c is
+// read by amax workgroup c mod kAmaxGrid and cast by workgroup c, both on XCD
+// c mod 8) and its grid.  Aligned x: chunks of the lane vectors; otherwise
+// chunks of the aligned 16-byte vectors that cover x (the shifted stream).
+struct AmaxPlan {
+    int K;
+    int grid;
+};
+template <int DT> AmaxPlan amax_plan(const void* x, int64_t n) {
     constexpr int VE = LaneVE<DT>::value;
-    int64_t units = (n + 255) / 256;
+    int64_t u1, units;
     if (al(x, 16)) {
-        const int64_t u1 = (n / VE + 255) / 256;
-        const int K = pick_flat_k(u1);
-        units = (u1 + K - 1) / K;
+        u1 = (n / VE + 255) / 256;
+        units = u1;
+    } else {   // the shifted cast pass takes kShiftK sub-steps per chunk
+        const int64_t mx = (int64_t)((uintptr_t)x & 15);
+        units = ((mx + n * ESize<DT>::value + 15) / 16 + 255) / 256;
+        return {kShiftK, (int)std::min(std::max<int64_t>((units + kShiftK - 1) / kShiftK, 1), kAmaxGrid)};
     }
-    return (int)std::min(std::max<int64_t>(units, 1), kAmaxGrid);
+    const int K = pick_flat_k(u1);
+    return {K, (int)std::min(std::max<int64_t>((units + K - 1) / K, 1), kAmaxGrid)};
 }
 
+template <int DT> int amax_partials_grid(const void* x, int64_t n) { return amax_plan<DT>(x, n).grid; }
+
 template <int DT> int run_amax_partials(const void* x, int64_t n, uint32_t* partial, hipStream_t st) {
-    constexpr int VE = LaneVE<DT>::value;
-    const int g = amax_partials_grid<DT>(x, n);
+    const AmaxPlan p = amax_plan<DT>(x, n);
+    const int g = p.grid;
     if (al(x, 16)) {
-        const int K = pick_flat_k((n / VE + 255) / 256);
-        if (K == 8) k_amax<DT, true, 8, false, true><<<g, kThreads, 0, st>>>(x, n, partial, 0);
-        else if (K == 4) k_amax<DT, true, 4, false, true><<<g, kThreads, 0, st>>>(x, n, partial, 0);
+        if (p.K == 8) k_amax<DT, true, 8, false, true><<<g, kThreads, 0, st>>>(x, n, partial, 0);
+        else if (p.K == 4) k_amax<DT, true, 4, false, true><<<g, kThreads, 0, st>>>(x, n, partial, 0);
         else k_amax<DT, true, 2, false, true><<<g, kThreads, 0, st>>>(x, n, partial, 0);
     } else {
-        k_amax<DT, false, kAmaxK, false, true><<<g, kThreads, 0, st>>>(x, n, partial, 0);
+        k_amax_shift<DT, kShiftK, false, true><<<g, kThreads, 0, st>>>(x, n, partial, 0);
     }
     return g;
 }
@@ -274,8 +227,7 @@ template <int FMT, int YDT> struct RunDequantFlat {
                 k_dequant_flat<FMT, YDT, MODE, true, decltype(K)::value, kNT><<<nb, kThreads, 0, st>>>(q, n, sinv, y);
             });
         } else {
-            k_dequant_flat<FMT, YDT, MODE, false, kFlatK, kNT><<<grid((n + 255) / 256), kThreads, 0, st>>>(q, n, sinv,
-                                                                                                           y);
+            launch_dequant_flat_shift(MODE, q, FMT, n, sinv, y, YDT, st);
         }
     }
     static void run(int mode, const uint8_t* q, int64_t n, const float* sinv, void* y, hipStream_t st) {
@@ -294,8 +246,7 @@ template <int DT> void run_pipeline_cast(const void* x, int64_t n, const uint32_
                                                                                         fmt_out);
         });
     } else {
-        k_pipeline_cast<DT, false, kFlatK, kNT><<<grid((n + 255) / 256), kThreads, 0, st>>>(x, n, partial, np, q,
-                                                                                             sinv, fmt_out);
+        launch_pipeline_cast_shift(x, DT, n, partial, np, q, sinv, fmt_out, st);
     }
 }
 
@@ -307,7 +258,7 @@ template <int YDT> void run_dequant_pipeline(const uint8_t* q, int64_t n, const 
             k_dequant_pipeline<YDT, true, decltype(K)::value, kNT><<<nb, kThreads, 0, st>>>(q, n, sinv, fmt, y);
         });
     } else {
-        k_dequant_pipeline<YDT, false, kFlatK, kNT><<<grid((n + 255) / 256), kThreads, 0, st>>>(q, n, sinv, fmt, y);
+        launch_dequant_pipeline_shift(q, n, sinv, fmt, y, YDT, st);
     }
 }
 
@@ -328,13 +279,16 @@ template <int FMT, int YDT> struct RunDequantPacked {
 template <int FMT, int YDT> struct RunDequantRows {
     static void run(const uint8_t* q, int64_t rows, int64_t cols, const float* sinv, void* y, hipStream_t st) {
         constexpr int VE = LaneVE<YDT>::value;
-        const bool vec = (cols % VE == 0) && al(q, 4) && al(y, 16);
+        const bool whole = cols % VE == 0;   // no lane vector straddles two rows
+        const bool vec = whole && al(q, 4) && al(y, 16);
         const int64_t nvec = rows * (cols / VE);
         if (vec && nvec < (int64_t(1) << 32)) {
             const DivU32 dv = make_div((uint32_t)(cols / VE));
             launch_k(nvec, [&](auto K, unsigned nb) {
                 k_dequant_rows_flat<FMT, YDT, decltype(K)::value, kNT><<<nb, kThreads, 0, st>>>(q, nvec, sinv, y, dv);
             });
+        } else if (whole && nvec < (int64_t(1) << 32)) {
+            launch_dequant_rows_shift(q, FMT, rows, cols, sinv, y, YDT, st);
         } else if (vec) {
             k_dequant_rows<FMT, YDT, true, kNT><<<grid(rows), kThreads, 0, st>>>(q, rows, cols, sinv, y);
         } else {

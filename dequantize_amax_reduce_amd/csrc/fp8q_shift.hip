@@ -1,0 +1,151 @@
+// fp8q_shift.hip -- launchers of the shifted-stream kernels (fp8q_device.h,
+// "shifted streaming"), for views aligned to their element size only: a
+// tensor that starts a few elements into its buffer keeps 16-byte (or 8- /
+// 4-byte fp8) lane vectors and aligned accesses instead of falling back to
+// element-wise kernels.  Every launcher takes chunks of kShiftK = 2 sub-steps
+// and a grid that covers the tensor, and dispatches on the input's dword
+// offset within its aligned vector (XDW), a compile-time constant of the
+// kernel.  A translation unit of its own, so that the build compiles it beside
+// fp8q_kernels.hip.
+#include "fp8q_host.h"
+
+namespace fp8q {
+namespace {
+
+// launch(KC<kShiftK>{}, grid) over nvec lane vectors: one size of chunk for
+// the shifted kernels (the 4- and 8-sub-step chunks of the vector kernels
+// would triple their instantiations)
+template <typename L> void launch_shift(int64_t nvec, L&& launch) {
+    launch(KC<kShiftK>{}, grid((nvec + kShiftK * 256 - 1) / (kShiftK * 256)));
+}
+
+template <int DT, int FMT> struct RunGroup128Shift {
+    static void run(const void* x, int64_t groups, uint8_t* q, float* sinv, hipStream_t st) {
+        constexpr int VE = LaneVE<DT>::value;
+        constexpr int64_t CH = kGroupK * (256 / (128 / VE));
+        const unsigned nb = grid((groups + CH - 1) / CH);
+        with_xdw<16>(x, [&](auto X) {
+            k_group128_shift<DT, FMT, kGroupK, decltype(X)::value><<<nb, kThreads, 0, st>>>(x, q, sinv, groups);
+        });
+    }
+};
+
+template <int DT, int FMT> struct RunTensorCastShift {
+    static void run(const void* x, int64_t n, const uint32_t* partial, int np, int pstride, uint8_t* q, float* sinv,
+                    hipStream_t st) {
+        constexpr int VE = LaneVE<DT>::value;
+        with_xdw<16>(x, [&](auto X) {
+            launch_shift((n + VE - 1) / VE, [&](auto K, unsigned nb) {
+                k_tensor_cast_shift<DT, FMT, decltype(K)::value, kNT, decltype(X)::value>
+                    <<<nb, kThreads, 0, st>>>(x, n, partial, np, pstride, q, sinv);
+            });
+        });
+    }
+};
+
+template <int DT, int FMT> struct RunCastGivenAmaxShift {
+    static void run(const void* x, int64_t n, const float* amax, uint8_t* q, float* scale_out, hipStream_t st) {
+        constexpr int VE = LaneVE<DT>::value;
+        with_xdw<16>(x, [&](auto X) {
+            launch_shift((n + VE - 1) / VE, [&](auto K, unsigned nb) {
+                k_cast_given_amax_shift<DT, FMT, decltype(K)::value, kNT, decltype(X)::value>
+                    <<<nb, kThreads, 0, st>>>(x, n, amax, q, scale_out);
+            });
+        });
+    }
+};
+
+template <int DT> void run_pipeline_cast_shift(const void* x, int64_t n, const uint32_t* partial, int np, uint8_t* q,
+                                               float* sinv, int32_t* fmt_out, hipStream_t st) {
+    constexpr int VE = LaneVE<DT>::value;
+    with_xdw<16>(x, [&](auto X) {
+        launch_shift((n + VE - 1) / VE, [&](auto K, unsigned nb) {
+            k_pipeline_cast_shift<DT, decltype(K)::value, kNT, decltype(X)::value>
+                <<<nb, kThreads, 0, st>>>(x, n, partial, np, q, sinv, fmt_out);
+        });
+    });
+}
+
+template <int FMT, int YDT> struct RunDequantFlatShift {
+    template <int MODE> static void go(const uint8_t* q, int64_t n, const float* sinv, void* y, hipStream_t st) {
+        constexpr int VE = LaneVE<YDT>::value;
+        with_xdw<VE>(q, [&](auto X) {
+            launch_shift((n + VE - 1) / VE, [&](auto K, unsigned nb) {
+                k_dequant_flat_shift<FMT, YDT, MODE, decltype(K)::value, kNT, decltype(X)::value>
+                    <<<nb, kThreads, 0, st>>>(q, n, sinv, y);
+            });
+        });
+    }
+    static void run(int mode, const uint8_t* q, int64_t n, const float* sinv, void* y, hipStream_t st) {
+        if (mode == 0) go<0>(q, n, sinv, y, st);
+        else if (mode == 3) go<3>(q, n, sinv, y, st);
+        else go<2>(q, n, sinv, y, st);
+    }
+};
+
+template <int YDT> void run_dequant_pipeline_shift(const uint8_t* q, int64_t n, const float* sinv, const int32_t* fmt,
+                                                   void* y, hipStream_t st) {
+    constexpr int VE = LaneVE<YDT>::value;
+    with_xdw<VE>(q, [&](auto X) {
+        launch_shift((n + VE - 1) / VE, [&](auto K, unsigned nb) {
+            k_dequant_pipeline_shift<YDT, decltype(K)::value, kNT, decltype(X)::value>
+                <<<nb, kThreads, 0, st>>>(q, n, sinv, fmt, y);
+        });
+    });
+}
+
+template <int FMT, int YDT> struct RunDequantRowsShift {
+    static void run(const uint8_t* q, int64_t rows, int64_t cols, const float* sinv, void* y, hipStream_t st) {
+        constexpr int VE = LaneVE<YDT>::value;
+        const int64_t nvec = rows * (cols / VE);
+        const DivU32 dv = make_div((uint32_t)(cols / VE));
+        with_xdw<VE>(q, [&](auto X) {
+            launch_shift(nvec, [&](auto K, unsigned nb) {
+                k_dequant_rows_shift<FMT, YDT, decltype(K)::value, kNT, decltype(X)::value>
+                    <<<nb, kThreads, 0, st>>>(q, nvec, sinv, y, dv);
+            });
+        });
+    }
+};
+
+}  // namespace
+
+void launch_group128_shift(const void* x, int dt, int64_t groups, int fmt, uint8_t* q, float* sinv, hipStream_t st) {
+    dispatch_dt_fmt<RunGroup128Shift>(dt, fmt, x, groups, q, sinv, st);
+}
+
+void launch_tensor_cast_shift(const void* x, int dt, int64_t n, int fmt, const uint32_t* partial, int np,
+                              int pstride, uint8_t* q, float* sinv, hipStream_t st) {
+    dispatch_dt_fmt<RunTensorCastShift>(dt, fmt, x, n, partial, np, pstride, q, sinv, st);
+}
+
+void launch_cast_given_amax_shift(const void* x, int dt, int64_t n, int fmt, const float* amax, uint8_t* q,
+                                  float* scale_out, hipStream_t st) {
+    dispatch_dt_fmt<RunCastGivenAmaxShift>(dt, fmt, x, n, amax, q, scale_out, st);
+}
+
+void launch_pipeline_cast_shift(const void* x, int dt, int64_t n, const uint32_t* partial, int np, uint8_t* q,
+                                float* sinv, int32_t* fmt_out, hipStream_t st) {
+    if (dt == kF32) run_pipeline_cast_shift<kF32>(x, n, partial, np, q, sinv, fmt_out, st);
+    else if (dt == kBF16) run_pipeline_cast_shift<kBF16>(x, n, partial, np, q, sinv, fmt_out, st);
+    else run_pipeline_cast_shift<kF16>(x, n, partial, np, q, sinv, fmt_out, st);
+}
+
+void launch_dequant_flat_shift(int mode, const uint8_t* q, int fmt, int64_t n, const float* sinv, void* y, int ydt,
+                               hipStream_t st) {
+    dispatch_fmt_ydt<RunDequantFlatShift>(fmt, ydt, mode, q, n, sinv, y, st);
+}
+
+void launch_dequant_pipeline_shift(const uint8_t* q, int64_t n, const float* sinv, const int32_t* fmt, void* y,
+                                   int ydt, hipStream_t st) {
+    if (ydt == kF32) run_dequant_pipeline_shift<kF32>(q, n, sinv, fmt, y, st);
+    else if (ydt == kBF16) run_dequant_pipeline_shift<kBF16>(q, n, sinv, fmt, y, st);
+    else run_dequant_pipeline_shift<kF16>(q, n, sinv, fmt, y, st);
+}
+
+void launch_dequant_rows_shift(const uint8_t* q, int fmt, int64_t rows, int64_t cols, const float* sinv, void* y,
+                               int ydt, hipStream_t st) {
+    dispatch_fmt_ydt<RunDequantRowsShift>(fmt, ydt, q, rows, cols, sinv, y, st);
+}
+
+}  // namespace fp8q

@@ -1,8 +1,8 @@
 """GPU parity on seeded random cases for every entry point: random shapes
 (ragged tails, odd row lengths, empty), element types, formats, magnitudes
 (10^-6 .. 10^6 with zero blocks) and buffer offsets (which switch between
-the vector kernels and the element-wise ones), each bit-exact against the
-CPU oracle (NaN by class)."""
+the vector kernels, the shifted ones and the element-wise ones), each
+bit-exact against the CPU oracle (NaN by class)."""
 import numpy as np
 import pytest
 import torch
