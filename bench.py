@@ -448,7 +448,35 @@ def _other_rows(fq, W, np, torch, dev, st, iters, log, HE, act, roundtrip):
     timed("group128_cast_bf16_e4m3fn_16384x7168 (one wavefront per group, 64 lanes x 2 bf16: "
           "fp8q_cast_per_group128_wave64)", Ra * Ca * 3 + Ra * (Ca // 128) * 4, Ra * Ca,
           lambda: fq.fp8q_cast_per_group128_wave64(act, qa8, sa8, "e4m3fn", stream=st))
-    del qa8, sa8
+
+    # the flat paths on the activation's element count, from aligned buffers and
+    # from views that start part-way into their buffers (the shifted stream):
+    # x and y two elements in, q two bytes in (for fp32 y, one element in)
+    na = act.numel()
+    xs = torch.empty(na + 8, dtype=torch.bfloat16, device=dev)
+    xs[2:2 + na].copy_(act.reshape(-1))
+    qs = torch.empty(na + 8, dtype=torch.uint8, device=dev)
+    ys = torch.empty(na + 8, dtype=torch.bfloat16, device=dev)
+    yf = torch.empty(na + 4, dtype=torch.float32, device=dev)
+    s1 = torch.empty(1, dtype=torch.float32, device=dev)
+    sr = torch.empty(Ra, dtype=torch.float32, device=dev)
+    wsv = torch.empty(fq.fp8q_per_tensor_workspace_bytes() // 4, dtype=torch.int32, device=dev)
+    with torch.cuda.stream(st):
+        fq.fp8q_cast_per_channel(act, qa8, sr, "e4m3fn", stream=st)
+    views = {"aligned": (act.reshape(-1), qs[:na], ys[:na], yf[:na]),
+             "views": (xs[2:2 + na], qs[2:2 + na], ys[2:2 + na], yf[1:1 + na])}
+    for tag, (xv, qv, yv, yfv) in views.items():
+        timed(f"per_tensor_cast_bf16_e4m3fn_16384x7168 ({tag}, amax pass + cast pass)", na * 5 + 4, na,
+              lambda: fq.fp8q_cast_per_tensor(xv, qv, s1, wsv, "e4m3fn", stream=st))
+        timed(f"per_tensor_dequant_e4m3fn_bf16_16384x7168 ({tag})", na * 3 + 4, na,
+              lambda: fq.fp8q_dequant_per_tensor(qv, s1, yv, "e4m3fn", stream=st))
+        timed(f"per_tensor_dequant_e4m3fn_f32_16384x7168 ({tag})", na * 5 + 4, na,
+              lambda: fq.fp8q_dequant_per_tensor(qv, s1, yfv, "e4m3fn", stream=st))
+        timed(f"group128_dequant_e4m3fn_bf16_16384x7168 ({tag})", na * 3 + Ra * (Ca // 128) * 4, na,
+              lambda: fq.fp8q_dequant_per_group128(qv.view(Ra, Ca), sa8, yv.view(Ra, Ca), "e4m3fn", stream=st))
+        timed(f"per_channel_dequant_e4m3fn_bf16_16384x7168 ({tag})", na * 3 + Ra * 4, na,
+              lambda: fq.fp8q_dequant_per_channel(qv.view(Ra, Ca), sr, yv.view(Ra, Ca), "e4m3fn", stream=st))
+    del qa8, sa8, xs, qs, ys, yf, views
 
     # pipeline p2p cast of the activation (bf16 [16384, 7168]) with the format
     # chosen on the device, and back to bf16

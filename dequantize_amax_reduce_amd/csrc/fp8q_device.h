@@ -28,6 +28,7 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "fp8q_launch.h"
 
@@ -503,36 +504,99 @@ __device__ __forceinline__ ShiftIO shift_io(const void* x, int64_t xbytes, void*
     return io;
 }
 
+// bytes [B, HI) of w to p + B .. (p 4W-byte aligned), in naturally aligned
+// pieces chosen at compile time
+template <int W, int B, int HI>
+__device__ __forceinline__ void store_bytes_ct(uint8_t* p, const Dw<W>& w) {
+    if constexpr (B < HI) {
+        constexpr int S = (B % 4 == 0 && B + 4 <= HI) ? 4 : ((B % 2 == 0 && B + 2 <= HI) ? 2 : 1);
+        const uint32_t v = w.d[B / 4] >> (8 * (B % 4));
+        if constexpr (S == 4) *(uint32_t*)(p + B) = v;
+        else if constexpr (S == 2) *(uint16_t*)(p + B) = (uint16_t)v;
+        else p[B] = (uint8_t)v;
+        store_bytes_ct<W, B + S, HI>(p, w);
+    }
+}
+
+// bytes [lo, 4W) (HEAD) or [0, lo) (!HEAD) of w, for a uniform 1 <= lo < 4W:
+// one compile-time piece sequence per value of lo, picked by uniform branches
+template <int W, bool HEAD, int... L>
+__device__ __forceinline__ void store_split_impl(uint8_t* p, const Dw<W>& w, int lo, std::integer_sequence<int, L...>) {
+    (void)((lo == L + 1 ? (HEAD ? store_bytes_ct<W, L + 1, 4 * W>(p, w) : store_bytes_ct<W, 0, L + 1>(p, w), true)
+                        : false) || ...);
+}
+template <int W, bool HEAD>
+__device__ __forceinline__ void store_split(uint8_t* p, const Dw<W>& w, int lo) {
+    store_split_impl<W, HEAD>(p, w, lo, std::make_integer_sequence<int, 4 * W - 1>{});
+}
+
 // the loads of one workgroup chunk (4 wave spans of K x 64 lane vectors)
 template <int IB, int K> struct ShiftLoads {
     Dw<IB / 4> a[K];
     Dw<IB / 4> e;   // lane 63: the aligned vector after the span
 };
 
+// Chunk c is interior when every access of the general path would be a full
+// aligned access inside the tensor: its input vectors and the one after them
+// lie in [mx, xhi), and all its lane vectors are valid with their output
+// words (and the last one's trailing word) inside y.  Every chunk but the
+// first and the last is; interior chunks skip the per-lane bounds checks.
+template <int IB, int OB, int K>
+__device__ __forceinline__ bool shift_interior(const ShiftIO& io, int64_t c) {
+    const int64_t v0 = c * (K * 256), v1 = v0 + K * 256;
+    return v0 * IB >= io.mx && (v1 + 1) * IB <= io.xhi && v1 <= io.nvec && (v1 + 1) * OB <= io.yhi;
+}
+
+// the first lane vector of this wave's span in chunk c (wave-uniform)
+template <int K> __device__ __forceinline__ int64_t span_first(int64_t c) {
+    return (c * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * (int64_t)(K * 64);
+}
+
 template <int IB, int ESZ, int K, bool NT>
 __device__ __forceinline__ void shift_load(ShiftLoads<IB, K>& L, const ShiftIO& io, int64_t c) {
     const int lane = threadIdx.x & 63;
-    const int64_t v0 = (c * 4 + (threadIdx.x >> 6)) * (int64_t)(K * 64);
+    const int64_t v0 = span_first<K>(c);
+    L.e = dw_zero<IB / 4>();
+    const int64_t c0 = c * (K * 256), c1 = c0 + K * 256;   // the chunk's aligned input vectors [c0, c1]
+    if (c0 * IB >= io.mx && (c1 + 1) * IB <= io.xhi) {     // uniform: all of them inside x, full loads
+        const char* base = io.xa + v0 * IB;   // wave-uniform; each lane adds a 32-bit offset
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const char* p = base + (uint32_t)((k * 64 + lane) * IB);
+            if constexpr (IB == 16) {
+                const v4u t = ld16<NT>(p);
+                L.a[k].d[0] = t.x; L.a[k].d[1] = t.y; L.a[k].d[2] = t.z; L.a[k].d[3] = t.w;
+            } else if constexpr (IB == 8) {
+                const v2u t = ld8<NT>(p);
+                L.a[k].d[0] = t.x; L.a[k].d[1] = t.y;
+            } else {
+                L.a[k].d[0] = ld4<NT>(p);
+            }
+        }
+        if (io.mx != 0 && lane == 63) L.e = aligned_vec<IB, ESZ, NT>(io.xa, v0 + K * 64, io.mx, io.xhi);
+        return;
+    }
 #pragma unroll
     for (int k = 0; k < K; ++k) L.a[k] = aligned_vec<IB, ESZ, NT>(io.xa, v0 + k * 64 + lane, io.mx, io.xhi);
-    L.e = dw_zero<IB / 4>();
     if (io.mx != 0 && lane == 63) L.e = aligned_vec<IB, ESZ, NT>(io.xa, v0 + K * 64, io.mx, io.xhi);
 }
 
 // Convert and store one loaded chunk: op(in, v, valid, k) maps lane vector
 // v's input (IB bytes; sub-step k) to its output (OB bytes); it runs in every
 // lane, valid or not (a lane past the end sees zeros and must not read scale
-// arrays with v).  Lanes away from the span's ends and the output's end take
-// one full aligned store; the rest go through one rarely taken edge block.
-// XDW = (input address mod IB) / 4, fixed at compile time: the funnel's dword
-// selection is then static and only the next lane's dwords 0..XDW move.
-template <int IB, int OB, int K, bool NT, int XDW, typename Op>
-__device__ __forceinline__ void shift_convert(const ShiftLoads<IB, K>& L, const ShiftIO& io, int64_t c, Op&& op) {
+// arrays with v).  XDW = (input address mod IB) / 4, fixed at compile time:
+// the funnel's dword selection is then static and only the next lane's dwords
+// 0..XDW move.  Interior chunks store full words from a wave-uniform base,
+// with the span's first and last lanes writing compile-time piece sequences;
+// the first and last chunk take the general path, which checks every lane.
+template <int IB, int OB, int K, bool NT, int XDW, bool INTERIOR, typename Op>
+__device__ __forceinline__ void shift_convert_path(const ShiftLoads<IB, K>& L, const ShiftIO& io, int64_t c, Op& op) {
     static_assert(XDW >= 0 && XDW < IB / 4, "input dword offset");
     constexpr int IW = IB / 4, OW = OB / 4;
     const int lane = threadIdx.x & 63;
-    const int64_t v0 = (c * 4 + (threadIdx.x >> 6)) * (int64_t)(K * 64);
-    Dw<OW> carry = dw_zero<OW>();   // lane 63's output at the previous sub-step
+    const int64_t v0 = span_first<K>(c);
+    const int od0 = (OB - io.my) >> 2;   // the first of the previous lane's output dwords needed (my != 0)
+    Dw<OW> carry = dw_zero<OW>();        // lane 63's output at the previous sub-step
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         Dw<IW> in = L.a[k];
@@ -540,7 +604,7 @@ __device__ __forceinline__ void shift_convert(const ShiftLoads<IB, K>& L, const 
             Dw<IW> nx = dw_zero<IW>();
 #pragma unroll
             for (int d = 0; d <= XDW; ++d) {
-                const uint32_t sh = from_next_lane(L.a[k].d[d]);
+                const uint32_t sh = from_next_lane(L.a[k].d[d]);   // straight-line, every lane active
                 uint32_t last = L.e.d[d];
                 if (k + 1 < K) last = lane_value(L.a[(k + 1) % K].d[d], 0);   // k is a constant here
                 nx.d[d] = lane == 63 ? last : sh;
@@ -548,45 +612,62 @@ __device__ __forceinline__ void shift_convert(const ShiftLoads<IB, K>& L, const 
             in = funnel_static<IW, XDW>(L.a[k], nx, io.mx & 3);
         }
         const int64_t v = v0 + k * 64 + lane;
-        const bool valid = v < io.nvec;
+        const bool valid = INTERIOR || v < io.nvec;
         const Dw<OW> out = op(in, v, valid, k);
-        const int64_t ob = v * OB;   // the aligned output word at ya + ob ends inside this lane's output
+        uint8_t* const wbase = io.ya + (v0 + k * 64) * OB;   // wave-uniform
+        uint8_t* const wq = wbase + (uint32_t)(lane * OB);    // the aligned word ending inside this lane's output
         if (io.my == 0) {
-            if (valid) {
-                const int64_t hi = io.yhi - ob;
-                if (hi >= OB) store_full<OW, NT>(io.ya + ob, out);
-                else store_word<OW, NT>(io.ya + ob, out, 0, (int)hi);
+            if (INTERIOR) {
+                store_full<OW, NT>(wq, out);
+            } else if (valid) {
+                const int64_t hi = io.yhi - v * OB;
+                if (hi >= OB) store_full<OW, NT>(wq, out);
+                else store_word<OW, NT>(wq, out, 0, (int)hi);
             }
             continue;
         }
-        Dw<OW> pv;
+        Dw<OW> pv = dw_zero<OW>();
 #pragma unroll
         for (int d = 0; d < OW; ++d) {
-            const uint32_t sh = from_prev_lane(out.d[d]);
-            pv.d[d] = lane == 0 ? carry.d[d] : sh;
+            if (d >= od0) {   // uniform
+                const uint32_t sh = from_prev_lane(out.d[d]);
+                pv.d[d] = lane == 0 ? carry.d[d] : sh;
+            }
         }
-        if (valid) {
-            const Dw<OW> w = funnel<OW>(pv, out, OB - io.my);
-            const int64_t hi = io.yhi - ob;
-            const bool head = lane == 0 && k == 0;                           // no previous lane's bytes here
-            const bool tail = (lane == 63 && k == K - 1) || v == io.nvec - 1;   // own trailing bytes too
+        const Dw<OW> w = funnel<OW>(pv, out, OB - io.my);
+        const bool head = lane == 0 && k == 0;                    // no previous lane's bytes here
+        if (INTERIOR) {
+            if (head) store_split<OW, true>(wq, w, io.my);
+            else store_full<OW, NT>(wq, w);
+            if (lane == 63 && k == K - 1)                          // own trailing bytes
+                store_split<OW, false>(wq + OB, funnel<OW>(out, dw_zero<OW>(), OB - io.my), io.my);
+        } else if (valid) {
+            const int64_t hi = io.yhi - v * OB;
+            const bool tail = (lane == 63 && k == K - 1) || v == io.nvec - 1;
             if (!head && !tail && hi >= OB) {
-                store_full<OW, NT>(io.ya + ob, w);
+                store_full<OW, NT>(wq, w);
             } else {
                 const int lo = head ? io.my : 0;
-                if (lo < hi) store_word<OW, NT>(io.ya + ob, w, lo, hi < OB ? (int)hi : OB);
+                if (lo < hi) store_word<OW, NT>(wq, w, lo, hi < OB ? (int)hi : OB);
                 const int64_t hi2 = hi - OB;
                 if (tail && hi2 > 0) {
                     const Dw<OW> t = funnel<OW>(out, dw_zero<OW>(), OB - io.my);
-                    store_word<OW, NT>(io.ya + ob + OB, t, 0, hi2 < io.my ? (int)hi2 : io.my);
+                    store_word<OW, NT>(wq + OB, t, 0, hi2 < io.my ? (int)hi2 : io.my);
                 }
             }
         }
         if (k + 1 < K) {
 #pragma unroll
-            for (int d = 0; d < OW; ++d) carry.d[d] = lane_value(out.d[d], 63);
+            for (int d = 0; d < OW; ++d)
+                if (d >= od0) carry.d[d] = lane_value(out.d[d], 63);   // uniform condition
         }
     }
+}
+
+template <int IB, int OB, int K, bool NT, int XDW, typename Op>
+__device__ __forceinline__ void shift_convert(const ShiftLoads<IB, K>& L, const ShiftIO& io, int64_t c, Op&& op) {
+    if (shift_interior<IB, OB, K>(io, c)) shift_convert_path<IB, OB, K, NT, XDW, true>(L, io, c, op);   // uniform
+    else shift_convert_path<IB, OB, K, NT, XDW, false>(L, io, c, op);
 }
 
 // ===========================================================================

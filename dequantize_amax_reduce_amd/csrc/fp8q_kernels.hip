@@ -1,7 +1,9 @@
 // fp8q_kernels.hip -- host-side launchers of the FP8 scaled-cast kernels
 // (fp8q_device.h) for gfx950.  Each launcher picks the vector kernel when the
-// pointers and shape allow 16-byte lane vectors and an element-wise kernel
-// otherwise; both produce identical bits.
+// pointers and shape allow 16-byte lane vectors, the shifted-stream kernel
+// (fp8q_shift.hip) for the flat operations when a pointer is aligned only to
+// its element size, and an element-wise kernel otherwise; all produce
+// identical bits.
 //
 // Launch configuration (MI355X: 256 CUs in 8 XCDs, 64-wide wavefronts),
 // chosen by sweeping K, grid size and the non-temporal hint on the
