@@ -474,6 +474,8 @@ def _other_rows(fq, W, np, torch, dev, st, iters, log, HE, act, roundtrip):
               lambda: fq.fp8q_dequant_per_tensor(qv, s1, yfv, "e4m3fn", stream=st))
         timed(f"group128_dequant_e4m3fn_bf16_16384x7168 ({tag})", na * 3 + Ra * (Ca // 128) * 4, na,
               lambda: fq.fp8q_dequant_per_group128(qv.view(Ra, Ca), sa8, yv.view(Ra, Ca), "e4m3fn", stream=st))
+        timed(f"per_channel_cast_bf16_e4m3fn_16384x7168 ({tag})", na * 3 + Ra * 4, na,
+              lambda: fq.fp8q_cast_per_channel(xv.view(Ra, Ca), qv.view(Ra, Ca), sr, "e4m3fn", stream=st))
         timed(f"per_channel_dequant_e4m3fn_bf16_16384x7168 ({tag})", na * 3 + Ra * 4, na,
               lambda: fq.fp8q_dequant_per_channel(qv.view(Ra, Ca), sr, yv.view(Ra, Ca), "e4m3fn", stream=st))
     del qa8, sa8, xs, qs, ys, yf, views

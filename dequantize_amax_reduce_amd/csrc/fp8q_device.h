@@ -1261,6 +1261,55 @@ k_channel_reg(const void* __restrict__ x, int64_t rows, int64_t cols, uint8_t* _
     }
 }
 
+// The per-channel cast of a view aligned only to its element size (cols %
+// VE == 0, so every row has the view's offset within its 16-byte vectors):
+// one workgroup per row, the row a shifted stream of one chunk (K x 256 >=
+// cols / VE lane vectors).  The row's amax comes straight from the aligned
+// loads (a max of |x| ignores the zeros outside the row); the cast then
+// realigns and stores like the flat shifted casts.
+template <int DT, int FMT, int K, int XDW>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_num_sgpr(96)))
+k_channel_shift(const void* __restrict__ x, int64_t rows, int64_t cols, uint8_t* __restrict__ q,
+                float* __restrict__ sinv_out) {
+    __shared__ uint32_t lds[4];
+    constexpr int VE = LaneVE<DT>::value;
+    constexpr int ESZ = ESize<DT>::value;
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+        const ShiftIO io = shift_io<16, VE>((const char*)x + r * cols * ESZ, cols * ESZ, q + r * cols, cols, cols / VE);
+        ShiftLoads<16, K> L;
+        shift_load<16, ESZ, K, true>(L, io, 0);
+        HpVec<DT> h;
+        h.r = v4u{L.e.d[0], L.e.d[1], L.e.d[2], L.e.d[3]};
+        uint32_t m = h.absmax_bits();
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            h.r = v4u{L.a[k].d[0], L.a[k].d[1], L.a[k].d[2], L.a[k].d[3]};
+            m = umax(m, h.absmax_bits());
+        }
+        m = block_max256(m, lds);
+        float scale, sinv;
+        channel_scale<FMT>(m, scale, sinv);
+        if (threadIdx.x == 0) sinv_out[r] = sinv;
+        const bool saturate = needs_saturation(m, scale);   // uniform
+        shift_convert<16, VE, K, true, XDW>(L, io, 0, [&](const Dw<4>& in, int64_t, bool, int) {
+            HpVec<DT> v;
+            v.r = v4u{in.d[0], in.d[1], in.d[2], in.d[3]};
+            float f[VE];
+            v.widen(f);
+            float p[VE];
+#pragma unroll
+            for (int e = 0; e < VE; ++e) {
+                p[e] = f[e] * scale;
+                if (saturate) p[e] = sat<FMT>(p[e]);
+            }
+            Dw<VE / 4> o;
+            o.d[0] = enc4<FMT>(p[0], p[1], p[2], p[3]);
+            if constexpr (VE == 8) o.d[1] = enc4<FMT>(p[4], p[5], p[6], p[7]);
+            return o;
+        });
+    }
+}
+
 // k_channel_reg for RPB consecutive rows per workgroup trip: all their loads
 // are issued before the one reduction barrier, so short rows keep more bytes
 // in flight per workgroup (bf16 [4096, 4096]: 10.7 us with two rows per trip

@@ -115,6 +115,10 @@ void launch_dequant_flat_shift(int mode, const uint8_t* q, int fmt, int64_t n, c
                                hipStream_t st);
 void launch_dequant_pipeline_shift(const uint8_t* q, int64_t n, const float* sinv, const int32_t* fmt, void* y,
                                    int ydt, hipStream_t st);
+// the per-channel cast of rows of cols % VE == 0 and at most 2048 lane
+// vectors; returns false (launching nothing) for other rows
+bool launch_channel_shift(const void* x, int dt, int64_t rows, int64_t cols, int fmt, uint8_t* q, float* sinv,
+                          hipStream_t st);
 // per-channel: cols % VE == 0 and rows * cols / VE < 2^32
 void launch_dequant_rows_shift(const uint8_t* q, int fmt, int64_t rows, int64_t cols, const float* sinv, void* y,
                                int ydt, hipStream_t st);

@@ -146,7 +146,9 @@ template <int DT, int FMT> struct RunChannel {
         // longer rows: two vector passes over the row (fp32 [256, 131072]: 46 us
         // against 347 us element-wise; bf16 [4000, 16400]: 44 against 120 us)
         else if (vec) k_channel_2pass_vec<DT, FMT, 8, kNT><<<nb, kThreads, 0, st>>>(x, rows, cols, q, sinv);
-        else k_channel_2pass<DT, FMT><<<nb, kThreads, 0, st>>>(x, rows, cols, q, sinv);
+        // views aligned only to their element size: the shifted stream per row
+        else if (!launch_channel_shift(x, DT, rows, cols, FMT, q, sinv, st))
+            k_channel_2pass<DT, FMT><<<nb, kThreads, 0, st>>>(x, rows, cols, q, sinv);
     }
 };
 

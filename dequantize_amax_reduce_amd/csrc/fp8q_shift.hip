@@ -108,7 +108,29 @@ template <int FMT, int YDT> struct RunDequantRowsShift {
     }
 };
 
+template <int DT, int FMT> struct RunChannelShift {
+    static void run(const void* x, int64_t rows, int64_t cols, uint8_t* q, float* sinv, hipStream_t st, bool* done) {
+        constexpr int VE = LaneVE<DT>::value;
+        const int64_t nvec = cols / VE;
+        *done = cols % VE == 0 && nvec <= 2048;
+        if (!*done) return;
+        with_xdw<16>(x, [&](auto X) {
+            constexpr int XD = decltype(X)::value;
+            if (nvec <= 512) k_channel_shift<DT, FMT, 2, XD><<<grid(rows), kThreads, 0, st>>>(x, rows, cols, q, sinv);
+            else if (nvec <= 1024) k_channel_shift<DT, FMT, 4, XD><<<grid(rows), kThreads, 0, st>>>(x, rows, cols, q, sinv);
+            else k_channel_shift<DT, FMT, 8, XD><<<grid(rows), kThreads, 0, st>>>(x, rows, cols, q, sinv);
+        });
+    }
+};
+
 }  // namespace
+
+bool launch_channel_shift(const void* x, int dt, int64_t rows, int64_t cols, int fmt, uint8_t* q, float* sinv,
+                          hipStream_t st) {
+    bool done = false;
+    dispatch_dt_fmt<RunChannelShift>(dt, fmt, x, rows, cols, q, sinv, st, &done);
+    return done;
+}
 
 void launch_group128_shift(const void* x, int dt, int64_t groups, int fmt, uint8_t* q, float* sinv, hipStream_t st) {
     dispatch_dt_fmt<RunGroup128Shift>(dt, fmt, x, groups, q, sinv, st);

@@ -188,3 +188,25 @@ def test_tensor_cast_and_dequant_fat_chunks_shifted(dtype):
         assert_fp8_equal(host(q), wq, "e4m3fn", f"q {dtype} n={n}")
         assert_f32_equal(host(s), wsi, f"scale_inv {dtype} n={n}")
         assert_hp_equal(host(y), oracle.dequant_per_tensor(wq, "e4m3fn", wsi, dtype), dtype, f"y {dtype} n={n}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_channel_cast_every_offset(dtype):
+    """The per-channel cast of views: each row a shifted stream (rows of 1000,
+    7168 and 16000 elements take chunks of 2, 4 and 8 sub-steps; 1004-element
+    16-bit rows are not whole lane vectors and take the element-wise kernel)."""
+    shapes = ((17, 1000, 21), (9, 7168, 22), (5, 16000, 23), (6, 1004, 24))
+    for rows, cols, seed in shapes:
+        x = _values(rows * cols, dtype, seed).reshape(rows, cols)
+        ref = {f: oracle.cast_per_channel(x, dtype, f) for f in FMTS}
+        offs = _offsets(dtype) if cols == 1000 else [(1, 3), (2, 6), (16 // ESZ[dtype] - 1, 7)]
+        for i, (xo, qo) in enumerate(offs):
+            fmt = FMTS[i % 2]
+            print(f"[case] per-channel cast {dtype} {fmt} {rows}x{cols} x+{xo} q+{qo}", flush=True)
+            q = _empty((rows, cols), torch.uint8, qo)
+            s = G.empty(rows, dtype=torch.float32, device="cuda:0")
+            fq.fp8q_cast_per_channel(_placed(x, dtype, xo), q, s, fmt)
+            torch.cuda.synchronize()
+            wq, ws = ref[fmt]
+            assert_fp8_equal(host(q), wq, fmt, f"channel q {dtype} {rows}x{cols} x+{xo} q+{qo}")
+            assert_f32_equal(host(s), ws, f"channel scale_inv {dtype} {rows}x{cols} x+{xo} q+{qo}")
