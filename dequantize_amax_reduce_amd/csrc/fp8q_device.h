@@ -841,43 +841,37 @@ k_group128_shift(const void* __restrict__ x, uint8_t* __restrict__ q, float* __r
 // i * kAmaxSlotStride, one slot per 128-byte line.  Device-scope atomics
 // serialise per cache line, so slots sharing a line gain nothing.
 
-// VEC (x 16-B aligned): chunks of K sub-steps x 256 lane vectors per
-// workgroup trip; the n % VE tail element-wise by workgroup 0.
-// Stage 2: with PART, workgroup b stores its result to amax_bits[b] (one
+// x 16-B aligned (k_amax_shift below serves the rest): chunks of K sub-steps
+// x 256 lane vectors per workgroup trip; the n % VE tail element-wise by
+// workgroup 0.  Stage 2: with PART, workgroup b stores its result to amax_bits[b] (one
 // partial per workgroup, every workgroup writes, so nothing needs clearing
 // and the consumer folds the partials); otherwise an atomic max of each
 // workgroup's result into one of `nslots` amax slots (workgroup b uses slot
 // b % nslots).
-template <int DT, bool VEC, int K, bool NT, bool PART = false>
+template <int DT, int K, bool NT, bool PART = false>
 __global__ void __launch_bounds__(256)
 k_amax(const void* __restrict__ x, int64_t n, uint32_t* __restrict__ amax_bits, int nslots) {
     __shared__ uint32_t lds[4];
     constexpr int VE = LaneVE<DT>::value;
     constexpr int ESZ = ESize<DT>::value;
     uint32_t m = 0;
-    int64_t done = 0;
-    if constexpr (VEC) {
-        const int64_t nvec = n / VE;
-        const int64_t nchunks = (nvec + K * 256 - 1) / (K * 256);
-        for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
-            HpVec<DT> v[K];
+    const int64_t nvec = n / VE;
+    const int64_t nchunks = (nvec + K * 256 - 1) / (K * 256);
+    for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+        HpVec<DT> v[K];
 #pragma unroll
-            for (int k = 0; k < K; ++k) {
-                const int64_t vi = (c * K + k) * 256 + threadIdx.x;
-                if (vi < nvec) v[k].template load<NT>((const char*)x + vi * VE * ESZ);
-            }
-#pragma unroll
-            for (int k = 0; k < K; ++k) {
-                const int64_t vi = (c * K + k) * 256 + threadIdx.x;
-                if (vi < nvec) m = umax(m, v[k].absmax_bits());
-            }
+        for (int k = 0; k < K; ++k) {
+            const int64_t vi = (c * K + k) * 256 + threadIdx.x;
+            if (vi < nvec) v[k].template load<NT>((const char*)x + vi * VE * ESZ);
         }
-        done = nvec * VE;
-        if (blockIdx.x == 0 && done + threadIdx.x < n) m = umax(m, absbits1<DT>(x, done + threadIdx.x));
-    } else {
-        for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-            m = umax(m, absbits1<DT>(x, i));
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int64_t vi = (c * K + k) * 256 + threadIdx.x;
+            if (vi < nvec) m = umax(m, v[k].absmax_bits());
+        }
     }
+    const int64_t done = nvec * VE;
+    if (blockIdx.x == 0 && done + threadIdx.x < n) m = umax(m, absbits1<DT>(x, done + threadIdx.x));
     m = block_max256(m, lds);
     if constexpr (PART) {
         if (threadIdx.x == 0) amax_bits[blockIdx.x] = m;
@@ -941,43 +935,37 @@ template <int FMT> __device__ __forceinline__ void tensor_scale(uint32_t amax_bi
     sinv = 1.0f / scale;
 }
 
-template <int DT, int FMT, bool VEC, int K, bool NT, bool SAT>
+// x 16-B aligned and q 4-byte aligned: chunks of K sub-steps x 256 lane
+// vectors per workgroup trip; the n % VE tail element-wise by workgroup 0
+template <int DT, int FMT, int K, bool NT, bool SAT>
 __device__ __forceinline__ void tensor_cast_body(const void* __restrict__ x, int64_t n, float scale,
                                                  uint8_t* __restrict__ q) {
     constexpr int VE = LaneVE<DT>::value;
     constexpr int ESZ = ESize<DT>::value;
-    if constexpr (VEC) {
-        const int64_t nvec = n / VE;
-        const int64_t nchunks = (nvec + K * 256 - 1) / (K * 256);
-        for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
-            HpVec<DT> v[K];
+    const int64_t nvec = n / VE;
+    const int64_t nchunks = (nvec + K * 256 - 1) / (K * 256);
+    for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+        HpVec<DT> v[K];
 #pragma unroll
-            for (int k = 0; k < K; ++k) {
-                const int64_t vi = (c * K + k) * 256 + threadIdx.x;
-                if (vi < nvec) v[k].template load<NT>((const char*)x + vi * VE * ESZ);
-            }
+        for (int k = 0; k < K; ++k) {
+            const int64_t vi = (c * K + k) * 256 + threadIdx.x;
+            if (vi < nvec) v[k].template load<NT>((const char*)x + vi * VE * ESZ);
+        }
 #pragma unroll
-            for (int k = 0; k < K; ++k) {
-                const int64_t vi = (c * K + k) * 256 + threadIdx.x;
-                if (vi < nvec) {
-                    float f[VE];
-                    v[k].widen(f);
-                    scale_encode_store<FMT, SAT, VE, NT>(f, scale, q + vi * VE);
-                }
+        for (int k = 0; k < K; ++k) {
+            const int64_t vi = (c * K + k) * 256 + threadIdx.x;
+            if (vi < nvec) {
+                float f[VE];
+                v[k].widen(f);
+                scale_encode_store<FMT, SAT, VE, NT>(f, scale, q + vi * VE);
             }
         }
-        const int64_t i = nvec * VE + threadIdx.x;
-        if (blockIdx.x == 0 && i < n) {
-            float p = load1<DT>(x, i) * scale;
-            if constexpr (SAT) p = sat<FMT>(p);
-            q[i] = enc1<FMT>(p);
-        }
-    } else {
-        for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-            float p = load1<DT>(x, i) * scale;
-            if constexpr (SAT) p = sat<FMT>(p);
-            q[i] = enc1<FMT>(p);
-        }
+    }
+    const int64_t i = nvec * VE + threadIdx.x;
+    if (blockIdx.x == 0 && i < n) {
+        float p = load1<DT>(x, i) * scale;
+        if constexpr (SAT) p = sat<FMT>(p);
+        q[i] = enc1<FMT>(p);
     }
 }
 
@@ -1024,27 +1012,22 @@ __device__ __forceinline__ void cast_chunks(HpVec<DT>* v, const void* __restrict
     }
 }
 
-// VEC: x 16-B aligned and q 4-byte aligned.  The amax is the max of the np
-// partials partial[0], partial[pstride], ...
-template <int DT, int FMT, bool VEC, int K, bool NT>
+// x 16-B aligned and q 4-byte aligned (k_tensor_cast_shift below serves the
+// rest).  The amax is the max of the np partials partial[0],
+// partial[pstride], ...
+template <int DT, int FMT, int K, bool NT>
 __global__ void __launch_bounds__(256)
 k_tensor_cast(const void* __restrict__ x, int64_t n, const uint32_t* __restrict__ partial, int np, int pstride,
               uint8_t* __restrict__ q, float* __restrict__ sinv_out) {
     __shared__ uint32_t lds[4];
     HpVec<DT> v[K];
-    if constexpr (VEC) chunk_load<DT, K, NT>(v, x, n / LaneVE<DT>::value, blockIdx.x);
+    chunk_load<DT, K, NT>(v, x, n / LaneVE<DT>::value, blockIdx.x);
     const uint32_t ab = fold_partials(partial, np, pstride, lds);
     float scale, sinv;
     tensor_scale<FMT>(ab, scale, sinv);
     if (blockIdx.x == 0 && threadIdx.x == 0) sinv_out[0] = sinv;
-    const bool saturate = needs_saturation(ab, scale);  // uniform
-    if constexpr (VEC) {
-        if (saturate) cast_chunks<DT, FMT, K, NT, true>(v, x, n, scale, q);
-        else cast_chunks<DT, FMT, K, NT, false>(v, x, n, scale, q);
-    } else {
-        if (saturate) tensor_cast_body<DT, FMT, false, K, NT, true>(x, n, scale, q);
-        else tensor_cast_body<DT, FMT, false, K, NT, false>(x, n, scale, q);
-    }
+    if (needs_saturation(ab, scale)) cast_chunks<DT, FMT, K, NT, true>(v, x, n, scale, q);   // uniform
+    else cast_chunks<DT, FMT, K, NT, false>(v, x, n, scale, q);
 }
 
 // Cast with a caller-supplied amax (ColossalAI fp8.py,
@@ -1052,13 +1035,13 @@ k_tensor_cast(const void* __restrict__ x, int64_t n, const uint32_t* __restrict_
 // across ranks): scale = fp8_max / amax, scale_out[0] = scale.  The given
 // amax need not bound this tensor's values, so the saturating path is always
 // taken.
-template <int DT, int FMT, bool VEC, int K, bool NT>
+template <int DT, int FMT, int K, bool NT>
 __global__ void __launch_bounds__(256)
 k_cast_given_amax(const void* __restrict__ x, int64_t n, const float* __restrict__ amax, uint8_t* __restrict__ q,
                   float* __restrict__ scale_out) {
     const float scale = Fp8Fmt<FMT>::max / amax[0];
     if (blockIdx.x == 0 && threadIdx.x == 0) scale_out[0] = scale;
-    tensor_cast_body<DT, FMT, VEC, K, NT, true>(x, n, scale, q);
+    tensor_cast_body<DT, FMT, K, NT, true>(x, n, scale, q);
 }
 
 // Pipeline p2p cast with the format chosen on the device (ColossalAI fp8.py,
@@ -1068,7 +1051,7 @@ k_cast_given_amax(const void* __restrict__ x, int64_t n, const float* __restrict
 // Workgroup 0 publishes scale_inv and the format word (0 = e4m3fn,
 // 1 = e5m2).  Every workgroup takes the same decision from the same
 // partials, so the branches are uniform.
-template <int DT, int FMT, bool VEC, int K, bool NT>
+template <int DT, int FMT, int K, bool NT>
 __device__ __forceinline__ void pipeline_cast_rest(HpVec<DT>* v, const void* __restrict__ x, int64_t n,
                                                    uint32_t ab, uint8_t* __restrict__ q,
                                                    float* __restrict__ sinv_out, int32_t* __restrict__ fmt_out) {
@@ -1078,28 +1061,24 @@ __device__ __forceinline__ void pipeline_cast_rest(HpVec<DT>* v, const void* __r
         sinv_out[0] = 1.0f / scale;
         fmt_out[0] = FMT;
     }
-    const bool saturate = needs_saturation(ab, scale);
-    if constexpr (VEC) {
-        if (saturate) cast_chunks<DT, FMT, K, NT, true>(v, x, n, scale, q);
-        else cast_chunks<DT, FMT, K, NT, false>(v, x, n, scale, q);
-    } else {
-        if (saturate) tensor_cast_body<DT, FMT, false, K, NT, true>(x, n, scale, q);
-        else tensor_cast_body<DT, FMT, false, K, NT, false>(x, n, scale, q);
-    }
+    if (needs_saturation(ab, scale)) cast_chunks<DT, FMT, K, NT, true>(v, x, n, scale, q);
+    else cast_chunks<DT, FMT, K, NT, false>(v, x, n, scale, q);
 }
 
-template <int DT, bool VEC, int K, bool NT>
+// x 16-B aligned and q 4-byte aligned (k_pipeline_cast_shift below serves
+// the rest)
+template <int DT, int K, bool NT>
 __global__ void __launch_bounds__(256)
 k_pipeline_cast(const void* __restrict__ x, int64_t n, const uint32_t* __restrict__ partial, int np,
                 uint8_t* __restrict__ q, float* __restrict__ sinv_out, int32_t* __restrict__ fmt_out) {
     __shared__ uint32_t lds[4];
     HpVec<DT> v[K];
-    if constexpr (VEC) chunk_load<DT, K, NT>(v, x, n / LaneVE<DT>::value, blockIdx.x);
+    chunk_load<DT, K, NT>(v, x, n / LaneVE<DT>::value, blockIdx.x);
     const uint32_t ab = fold_partials(partial, np, 1, lds);
     if (__uint_as_float(ab) > Fp8Fmt<kE4M3>::max)
-        pipeline_cast_rest<DT, kE5M2, VEC, K, NT>(v, x, n, ab, q, sinv_out, fmt_out);
+        pipeline_cast_rest<DT, kE5M2, K, NT>(v, x, n, ab, q, sinv_out, fmt_out);
     else
-        pipeline_cast_rest<DT, kE4M3, VEC, K, NT>(v, x, n, ab, q, sinv_out, fmt_out);
+        pipeline_cast_rest<DT, kE4M3, K, NT>(v, x, n, ab, q, sinv_out, fmt_out);
 }
 
 // The same casts for x aligned to its element size only or q to nothing:
@@ -1497,10 +1476,12 @@ __device__ __forceinline__ void dequant_flat_body(const uint8_t* __restrict__ q,
     }
 }
 
-template <int FMT, int YDT, int MODE, bool VEC, int K, bool NT>
+// q 4-byte aligned and y 16-B aligned (k_dequant_flat_shift below serves the
+// rest)
+template <int FMT, int YDT, int MODE, int K, bool NT>
 __global__ void __launch_bounds__(256)
 k_dequant_flat(const uint8_t* __restrict__ q, int64_t n, const float* __restrict__ sinv, void* __restrict__ y) {
-    dequant_flat_body<FMT, YDT, MODE, VEC, K, NT>(q, n, sinv, y, blockIdx.x, gridDim.x, blockIdx.x == 0);
+    dequant_flat_body<FMT, YDT, MODE, true, K, NT>(q, n, sinv, y, blockIdx.x, gridDim.x, blockIdx.x == 0);
 }
 
 // The flat dequants for q or y aligned to their element size only: the
@@ -1582,14 +1563,16 @@ k_dequant_packed(const uint8_t* __restrict__ slots, int64_t W, int64_t n, void* 
 // so the host never waits for it.  Every workgroup reads the same word, so the
 // branch is uniform.  A word other than e4m3fn (0) or e5m2 (1) gives NaN
 // everywhere.
-template <int YDT, bool VEC, int K, bool NT>
+// q 4-byte aligned and y 16-B aligned (k_dequant_pipeline_shift below serves
+// the rest).
+template <int YDT, int K, bool NT>
 __global__ void __launch_bounds__(256)
 k_dequant_pipeline(const uint8_t* __restrict__ q, int64_t n, const float* __restrict__ sinv,
                    const int32_t* __restrict__ fmt, void* __restrict__ y) {
     const int32_t f = fmt[0];
-    if (f == kE4M3) dequant_flat_body<kE4M3, YDT, 0, VEC, K, NT>(q, n, sinv, y, blockIdx.x, gridDim.x, blockIdx.x == 0);
+    if (f == kE4M3) dequant_flat_body<kE4M3, YDT, 0, true, K, NT>(q, n, sinv, y, blockIdx.x, gridDim.x, blockIdx.x == 0);
     else if (f == kE5M2)
-        dequant_flat_body<kE5M2, YDT, 0, VEC, K, NT>(q, n, sinv, y, blockIdx.x, gridDim.x, blockIdx.x == 0);
+        dequant_flat_body<kE5M2, YDT, 0, true, K, NT>(q, n, sinv, y, blockIdx.x, gridDim.x, blockIdx.x == 0);
     else
         for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
             store1<YDT>(y, i, __builtin_nanf(""));

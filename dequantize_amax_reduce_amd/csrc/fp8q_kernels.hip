@@ -92,10 +92,10 @@ template <int DT, int FMT> struct RunTensorCast {
         const bool vec = al(x, 16) && al(q, 4);
         if (vec && cached) {
             const unsigned nb = grid((n / VE + kFlatK * 256 - 1) / (kFlatK * 256));
-            k_tensor_cast<DT, FMT, true, kFlatK, false><<<nb, kThreads, 0, st>>>(x, n, partial, np, pstride, q, sinv);
+            k_tensor_cast<DT, FMT, kFlatK, false><<<nb, kThreads, 0, st>>>(x, n, partial, np, pstride, q, sinv);
         } else if (vec) {
             launch_k(n / VE, [&](auto K, unsigned nb) {
-                k_tensor_cast<DT, FMT, true, decltype(K)::value, kNT><<<nb, kThreads, 0, st>>>(x, n, partial, np,
+                k_tensor_cast<DT, FMT, decltype(K)::value, kNT><<<nb, kThreads, 0, st>>>(x, n, partial, np,
                                                                                                pstride, q, sinv);
             });
         } else {   // the shifted stream, with the amax pass's sub-steps per chunk (amax_plan)
@@ -109,7 +109,7 @@ template <int DT, int FMT> struct RunCastGivenAmax {
         constexpr int VE = LaneVE<DT>::value;
         if (al(x, 16) && al(q, 4)) {   // bf16 [4096, 4096]: 11.4 us with K = 4 against 12.1 with K = 2
             launch_k(n / VE, [&](auto K, unsigned nb) {
-                k_cast_given_amax<DT, FMT, true, decltype(K)::value, kNT><<<nb, kThreads, 0, st>>>(x, n, amax, q,
+                k_cast_given_amax<DT, FMT, decltype(K)::value, kNT><<<nb, kThreads, 0, st>>>(x, n, amax, q,
                                                                                                    scale_out);
             });
         } else {
@@ -165,7 +165,7 @@ template <int DT> void run_amax(const void* x, int64_t n, uint32_t* word, hipStr
     const int64_t cap = kAmaxGrid;
     if (al(x, 16)) {
         const int64_t chunks = (n / VE + kAmaxK * 256 - 1) / (kAmaxK * 256);
-        k_amax<DT, true, kAmaxK, kNT><<<(unsigned)std::min(std::max<int64_t>(chunks, 1), cap), kThreads, 0, st>>>(
+        k_amax<DT, kAmaxK, kNT><<<(unsigned)std::min(std::max<int64_t>(chunks, 1), cap), kThreads, 0, st>>>(
             x, n, word, 1);
     } else {
         const int64_t mx = (int64_t)((uintptr_t)x & 15);
@@ -214,9 +214,9 @@ template <int DT> int run_amax_partials(const void* x, int64_t n, uint32_t* part
     const AmaxPlan p = amax_plan<DT>(x, n);
     const int g = p.grid;
     if (al(x, 16)) {
-        if (p.K == 8) k_amax<DT, true, 8, false, true><<<g, kThreads, 0, st>>>(x, n, partial, 0);
-        else if (p.K == 4) k_amax<DT, true, 4, false, true><<<g, kThreads, 0, st>>>(x, n, partial, 0);
-        else k_amax<DT, true, 2, false, true><<<g, kThreads, 0, st>>>(x, n, partial, 0);
+        if (p.K == 8) k_amax<DT, 8, false, true><<<g, kThreads, 0, st>>>(x, n, partial, 0);
+        else if (p.K == 4) k_amax<DT, 4, false, true><<<g, kThreads, 0, st>>>(x, n, partial, 0);
+        else k_amax<DT, 2, false, true><<<g, kThreads, 0, st>>>(x, n, partial, 0);
     } else {
         k_amax_shift<DT, kShiftK, false, true><<<g, kThreads, 0, st>>>(x, n, partial, 0);
     }
@@ -228,7 +228,7 @@ template <int FMT, int YDT> struct RunDequantFlat {
         constexpr int VE = LaneVE<YDT>::value;
         if (al(q, 4) && al(y, 16)) {
             launch_k(n / VE, [&](auto K, unsigned nb) {
-                k_dequant_flat<FMT, YDT, MODE, true, decltype(K)::value, kNT><<<nb, kThreads, 0, st>>>(q, n, sinv, y);
+                k_dequant_flat<FMT, YDT, MODE, decltype(K)::value, kNT><<<nb, kThreads, 0, st>>>(q, n, sinv, y);
             });
         } else {
             launch_dequant_flat_shift(MODE, q, FMT, n, sinv, y, YDT, st);
@@ -246,7 +246,7 @@ template <int DT> void run_pipeline_cast(const void* x, int64_t n, const uint32_
     constexpr int VE = LaneVE<DT>::value;
     if (al(x, 16) && al(q, 4)) {   // the amax pass's sub-steps per chunk (RunTensorCast)
         launch_k(n / VE, [&](auto K, unsigned nb) {
-            k_pipeline_cast<DT, true, decltype(K)::value, kNT><<<nb, kThreads, 0, st>>>(x, n, partial, np, q, sinv,
+            k_pipeline_cast<DT, decltype(K)::value, kNT><<<nb, kThreads, 0, st>>>(x, n, partial, np, q, sinv,
                                                                                         fmt_out);
         });
     } else {
@@ -259,7 +259,7 @@ template <int YDT> void run_dequant_pipeline(const uint8_t* q, int64_t n, const 
     constexpr int VE = LaneVE<YDT>::value;
     if (al(q, 4) && al(y, 16)) {   // as the per-tensor dequant: [4096, 4096] -> bf16 10.3 us against 11.6
         launch_k(n / VE, [&](auto K, unsigned nb) {
-            k_dequant_pipeline<YDT, true, decltype(K)::value, kNT><<<nb, kThreads, 0, st>>>(q, n, sinv, fmt, y);
+            k_dequant_pipeline<YDT, decltype(K)::value, kNT><<<nb, kThreads, 0, st>>>(q, n, sinv, fmt, y);
         });
     } else {
         launch_dequant_pipeline_shift(q, n, sinv, fmt, y, YDT, st);
