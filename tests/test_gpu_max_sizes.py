@@ -7,7 +7,7 @@ generators; only the samples travel to the host.
 - per-128-group cast and dequant of bf16 [300000, 7168] (2.15e9 elements, > 2^31),
   then the cast again from views two elements into the same buffers
 - per-tensor cast and dequant of 2^32 + 37 bf16 elements with the maximum
-  planted beyond 2^32
+  planted beyond 2^32, then again from views part-way into their buffers
 - 128x128 block dequant of e4m3fn [4793491, 7168] (>= 2^32 lane vectors: the
   row-strip kernel), 34 GB of codes and 69 GB of bf16 output
 """
@@ -88,7 +88,7 @@ def test_group128_beyond_2_31_elements():
 def test_per_tensor_beyond_2_32_elements():
     n = (1 << 32) + 37
     peak = (1 << 32) + 5
-    _need(32)
+    _need(40)
     print(f"[case] per-tensor bf16 n={n}, maximum at {peak}", flush=True)
     x = torch.randn(n, generator=_gen(83), device=DEV, dtype=torch.bfloat16)
     x[peak] = -300.0                      # |x| of N(0, 1) stays far below 300 over 2^32 draws
@@ -110,13 +110,37 @@ def test_per_tensor_beyond_2_32_elements():
     wq, wsi = oracle.cast_per_tensor(xs, "bf16", "e5m2")
     assert_f32_equal(host(si), wsi, "scale_inv")
     assert_fp8_equal(qs, wq, "e5m2", "sampled q")
-    del x
+    # again from a view two elements into x, into codes one byte into their
+    # buffer: the shifted amax pass and cast pass, past 2^32 elements
+    nv = n - 2
+    xv = x[2:]
+    q2 = G.empty(n, dtype=torch.uint8, device=DEV)
+    qv = q2[1:1 + nv]
+    si2 = G.empty(1, dtype=torch.float32, device=DEV)
+    amax2 = G.empty(1, dtype=torch.float32, device=DEV)
+    print(f"[case] per-tensor bf16 shifted n={nv}", flush=True)
+    fq.fp8q_amax(xv, amax2)
+    fq.fp8q_cast_per_tensor(xv, qv, si2, ws, "e5m2")
+    torch.cuda.synchronize()
+    assert float(host(amax2)[0]) == 300.0
+    idv = np.unique(np.concatenate([[0, 1, peak - 2, nv - 37, nv - 5, nv - 1], rng.integers(0, nv, 4000),
+                                    rng.integers((1 << 32) - 2, nv, 30)]))
+    tv = torch.from_numpy(idv).to(DEV)
+    wqv, wsiv = oracle.cast_per_tensor(_bits(xv[tv]), "bf16", "e5m2")
+    assert_f32_equal(host(si2), wsiv, "shifted scale_inv")
+    assert_fp8_equal(_bits(qv[tv]), wqv, "e5m2", "shifted sampled q")
+    del x, xv
     torch.cuda.empty_cache()
     y = G.empty(n, dtype=torch.bfloat16, device=DEV)
     fq.fp8q_dequant_per_tensor(q, si, y, "e5m2")
     torch.cuda.synchronize()
     assert_hp_equal(_bits(y[ti]), oracle.dequant_per_tensor(wq, "e5m2", wsi, "bf16"), "bf16", "sampled y")
-    _free(q, y, ws, amax, si)
+    # the shifted dequant: those codes into an output one element into its buffer
+    yv = y[1:1 + nv]
+    fq.fp8q_dequant_per_tensor(qv, si2, yv, "e5m2")
+    torch.cuda.synchronize()
+    assert_hp_equal(_bits(yv[tv]), oracle.dequant_per_tensor(wqv, "e5m2", wsiv, "bf16"), "bf16", "shifted sampled y")
+    _free(q, q2, y, ws, amax, amax2, si, si2)
 
 
 def test_block_dequant_row_strip_path():
