@@ -536,20 +536,23 @@ template <int IB, int K> struct ShiftLoads {
     Dw<IB / 4> e;   // lane 63: the aligned vector after the span
 };
 
-// Chunk c is interior when every access of the general path would be a full
-// aligned access inside the tensor: its input vectors and the one after them
-// lie in [mx, xhi), and all its lane vectors are valid with their output
-// words (and the last one's trailing word) inside y.  Every chunk but the
-// first and the last is; interior chunks skip the per-lane bounds checks.
-template <int IB, int OB, int K>
-__device__ __forceinline__ bool shift_interior(const ShiftIO& io, int64_t c) {
-    const int64_t v0 = c * (K * 256), v1 = v0 + K * 256;
-    return v0 * IB >= io.mx && (v1 + 1) * IB <= io.xhi && v1 <= io.nvec && (v1 + 1) * OB <= io.yhi;
-}
-
 // the first lane vector of this wave's span in chunk c (wave-uniform)
 template <int K> __device__ __forceinline__ int64_t span_first(int64_t c) {
     return (c * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * (int64_t)(K * 64);
+}
+
+// This wave's span in chunk c is interior when every access of the general
+// path would be a full aligned access inside the tensor: its input vectors
+// and the one after them lie in [mx, xhi), and all its lane vectors are valid
+// with their output words (and the last one's trailing word) inside y.  The
+// test is per wave (its span's edge pieces are its own, whichever path its
+// neighbours take): in a flat stream only the waves at the two ends fail it,
+// and in a per-row stream of one chunk (the per-channel cast) only the
+// row's first and last waves.  Interior spans skip the per-lane bounds checks.
+template <int IB, int OB, int K>
+__device__ __forceinline__ bool shift_interior(const ShiftIO& io, int64_t c) {
+    const int64_t v0 = span_first<K>(c), v1 = v0 + K * 64;
+    return v0 * IB >= io.mx && (v1 + 1) * IB <= io.xhi && v1 <= io.nvec && (v1 + 1) * OB <= io.yhi;
 }
 
 template <int IB, int ESZ, int K, bool NT>
@@ -557,8 +560,8 @@ __device__ __forceinline__ void shift_load(ShiftLoads<IB, K>& L, const ShiftIO& 
     const int lane = threadIdx.x & 63;
     const int64_t v0 = span_first<K>(c);
     L.e = dw_zero<IB / 4>();
-    const int64_t c0 = c * (K * 256), c1 = c0 + K * 256;   // the chunk's aligned input vectors [c0, c1]
-    if (c0 * IB >= io.mx && (c1 + 1) * IB <= io.xhi) {     // uniform: all of them inside x, full loads
+    const int64_t v1 = v0 + K * 64;                    // the span's aligned input vectors [v0, v1]
+    if (v0 * IB >= io.mx && (v1 + 1) * IB <= io.xhi) {   // wave-uniform: all of them inside x, full loads
         const char* base = io.xa + v0 * IB;   // wave-uniform; each lane adds a 32-bit offset
 #pragma unroll
         for (int k = 0; k < K; ++k) {
@@ -586,9 +589,10 @@ __device__ __forceinline__ void shift_load(ShiftLoads<IB, K>& L, const ShiftIO& 
 // lane, valid or not (a lane past the end sees zeros and must not read scale
 // arrays with v).  XDW = (input address mod IB) / 4, fixed at compile time:
 // the funnel's dword selection is then static and only the next lane's dwords
-// 0..XDW move.  Interior chunks store full words from a wave-uniform base,
+// 0..XDW move.  Interior spans store full words from a wave-uniform base,
 // with the span's first and last lanes writing compile-time piece sequences;
-// the first and last chunk take the general path, which checks every lane.
+// the spans at the stream's ends take the general path, which checks every
+// lane.
 template <int IB, int OB, int K, bool NT, int XDW, bool INTERIOR, typename Op>
 __device__ __forceinline__ void shift_convert_path(const ShiftLoads<IB, K>& L, const ShiftIO& io, int64_t c, Op& op) {
     static_assert(XDW >= 0 && XDW < IB / 4, "input dword offset");
@@ -666,7 +670,7 @@ __device__ __forceinline__ void shift_convert_path(const ShiftLoads<IB, K>& L, c
 
 template <int IB, int OB, int K, bool NT, int XDW, typename Op>
 __device__ __forceinline__ void shift_convert(const ShiftLoads<IB, K>& L, const ShiftIO& io, int64_t c, Op&& op) {
-    if (shift_interior<IB, OB, K>(io, c)) shift_convert_path<IB, OB, K, NT, XDW, true>(L, io, c, op);   // uniform
+    if (shift_interior<IB, OB, K>(io, c)) shift_convert_path<IB, OB, K, NT, XDW, true>(L, io, c, op);   // per wave
     else shift_convert_path<IB, OB, K, NT, XDW, false>(L, io, c, op);
 }
 

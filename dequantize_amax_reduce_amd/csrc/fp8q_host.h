@@ -16,7 +16,7 @@ constexpr int64_t kAmaxGrid = kAmaxPartials;  // amax-pass workgroups (and parti
 constexpr int64_t kSumAmaxGrid = 8192;  // the reduce step's sum pass when it also folds the amax
 
 constexpr int kGroupK = 2;        // sub-steps per group-cast chunk
-constexpr int kShiftK = 2;        // sub-steps per chunk of the shifted kernels
+constexpr int kShiftK = 4;        // sub-steps per chunk of the shifted flat kernels
 constexpr int kFlatK = 2;         // sub-steps per flat chunk outside pick_flat_k's window
 constexpr int kAmaxK = 2;         // sub-steps per amax chunk
 constexpr int kBlockK = 2;        // sub-steps per block-dequant chunk

@@ -2,19 +2,27 @@
 // "shifted streaming"), for views aligned to their element size only: a
 // tensor that starts a few elements into its buffer keeps 16-byte (or 8- /
 // 4-byte fp8) lane vectors and aligned accesses instead of falling back to
-// element-wise kernels.  Every launcher takes chunks of kShiftK = 2 sub-steps
-// and a grid that covers the tensor, and dispatches on the input's dword
-// offset within its aligned vector (XDW), a compile-time constant of the
-// kernel.  A translation unit of its own, so that the build compiles it beside
-// fp8q_kernels.hip.
+// element-wise kernels.  The flat launchers take chunks of kShiftK = 4
+// sub-steps and a grid that covers the tensor (the group cast keeps the
+// aligned kernel's kGroupK, the per-channel cast one chunk per row).  Every
+// launcher dispatches on the input's dword offset within its aligned vector
+// (XDW), a compile-time constant of the kernel.  A translation unit of its
+// own, so that the build compiles it beside fp8q_kernels.hip.
 #include "fp8q_host.h"
 
 namespace fp8q {
 namespace {
 
 // launch(KC<kShiftK>{}, grid) over nvec lane vectors: one size of chunk for
-// the shifted kernels (the 4- and 8-sub-step chunks of the vector kernels
-// would triple their instantiations)
+// the shifted flat kernels.  Each wave's set-up (span geometry, edge tests,
+// the lane shuffles' boundary values) costs three to four times the scalar
+// work of an aligned kernel's, and a longer span spreads it over more bytes.
+// On the activation [16384, 7168], views two elements in, K = 4 against
+// K = 2: fp32 dequant 101.6 against 116.2 us (K = 8: 109.4), group dequant
+// 62.7 against 69.5, per-channel dequant 63.0 against 67.3, both passes of
+// the per-tensor cast 103.3 against 108.0, bf16 dequant 63.4 against 65.3.
+// A size-dependent K like the vector kernels' would multiply the
+// instantiations, already one per input dword offset.
 template <typename L> void launch_shift(int64_t nvec, L&& launch) {
     launch(KC<kShiftK>{}, grid((nvec + kShiftK * 256 - 1) / (kShiftK * 256)));
 }
