@@ -14,19 +14,19 @@ from gpu_util import G, assert_f32_equal, assert_fp8_equal, assert_hp_equal, dev
 pytestmark = pytest.mark.gpu
 
 
-def _sum(q, s, fmt, ydtype, average, requant, q_offset=0):
+def _sum(q, s, fmt, ydtype, average, requant, q_offset=0, y_offset=0, qo_offset=0):
     Wn, n = q.shape
     qb = G.empty(Wn * n + q_offset, dtype=torch.uint8, device="cuda:0")
     qb[q_offset:] = dev(q.reshape(-1))
     qd = qb[q_offset:].view(Wn, n)
-    y = empty_hp(n, ydtype)
-    print(f"[case] dequant_sum W={Wn} n={n} {fmt}->{ydtype} avg={average} requant={requant} q_off={q_offset}",
-          flush=True)
+    y = empty_hp(n + y_offset, ydtype)[y_offset:]
+    print(f"[case] dequant_sum W={Wn} n={n} {fmt}->{ydtype} avg={average} requant={requant} q_off={q_offset} "
+          f"y_off={y_offset} qo_off={qo_offset}", flush=True)
     if not requant:
         fq.fp8q_dequant_sum(qd, dev(s), y, fmt, average)
         torch.cuda.synchronize()
         return host(y), None, None
-    qo = G.empty(n, dtype=torch.uint8, device="cuda:0")
+    qo = G.empty(n + qo_offset, dtype=torch.uint8, device="cuda:0")[qo_offset:]
     so = G.full((1,), -3.0, dtype=torch.float32, device="cuda:0")
     ws = G.full((fq.fp8q_per_tensor_workspace_bytes() // 4,), 12345, dtype=torch.int32, device="cuda:0")
     fq.fp8q_dequant_sum_requant(qd, dev(s), y, qo, so, ws, fmt, average)
@@ -57,6 +57,18 @@ def test_dequant_sum_shapes(Wn, n, fmt, ydtype):
 def test_dequant_sum_unaligned(q_offset):
     q, s = W.received_chunks(3, 1000, "e5m2", seed=3)
     _check(q, s, "e5m2", "bf16", True, requant=True, q_offset=q_offset)
+
+
+@pytest.mark.parametrize("ydtype,y_offset,qo_offset", [("bf16", 1, 0), ("bf16", 3, 2), ("f32", 1, 1), ("f16", 2, 3)])
+def test_dequant_sum_requant_unaligned_outputs(ydtype, y_offset, qo_offset):
+    """y (the sum, which the re-cast reads) and the re-cast's codes as views
+    part-way into their buffers: the re-cast then takes the shifted cast
+    kernel, which folds the 64 amax slots (128 bytes apart) the sum left in
+    the workspace.  Sizes span several chunks of that kernel and a ragged
+    tail."""
+    for n in (1000, 300007):
+        q, s = W.received_chunks(4, n, "e5m2", seed=n % 101 + y_offset)
+        _check(q, s, "e5m2", ydtype, True, requant=True, y_offset=y_offset, qo_offset=qo_offset)
 
 
 def test_dequant_sum_special_values():
