@@ -344,6 +344,17 @@ template <int W> __device__ __forceinline__ Dw<W> dw_zero() {
     return r;
 }
 
+// w with its bytes [0, nb) cleared (0 <= nb <= 4W)
+template <int W> __device__ __forceinline__ Dw<W> zero_below(Dw<W> w, int nb) {
+#pragma unroll
+    for (int t = 0; t < W; ++t) {
+        const int k = nb - 4 * t;   // bytes of dword t to clear, from its low end
+        if (k >= 4) w.d[t] = 0u;
+        else if (k > 0) w.d[t] &= ~0u << (8 * k);
+    }
+    return w;
+}
+
 // whole-wave DPP lane shifts (bound_ctrl off: the lane with no source keeps 0)
 __device__ __forceinline__ uint32_t from_next_lane(uint32_t v) {   // lane t <- lane t + 1 (wave_shl:1)
     return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x130, 0xF, 0xF, false);
@@ -542,26 +553,31 @@ template <int K> __device__ __forceinline__ int64_t span_first(int64_t c) {
 }
 
 // This wave's span in chunk c is interior when every access of the general
-// path would be a full aligned access inside the tensor: its input vectors
-// and the one after them lie in [mx, xhi), and all its lane vectors are valid
-// with their output words (and the last one's trailing word) inside y.  The
-// test is per wave (its span's edge pieces are its own, whichever path its
+// path would be a full aligned access to readable memory: its input vectors
+// and the one after them lie in [rlo, xhi), and all its lane vectors are
+// valid with their output words (and the last one's trailing word) inside y.
+// rlo is the lowest readable byte from xa: the stream's start mx, or 0 where
+// the bytes before the stream belong to the same tensor (rows after the first
+// of a per-row stream); the realignment never uses bytes below mx.  The test
+// is per wave (its span's edge pieces are its own, whichever path its
 // neighbours take): in a flat stream only the waves at the two ends fail it,
 // and in a per-row stream of one chunk (the per-channel cast) only the
-// row's first and last waves.  Interior spans skip the per-lane bounds checks.
+// row's last wave, and the first row's first.  Interior spans skip the
+// per-lane bounds checks.
 template <int IB, int OB, int K>
-__device__ __forceinline__ bool shift_interior(const ShiftIO& io, int64_t c) {
+__device__ __forceinline__ bool shift_interior(const ShiftIO& io, int64_t c, int64_t rlo) {
     const int64_t v0 = span_first<K>(c), v1 = v0 + K * 64;
-    return v0 * IB >= io.mx && (v1 + 1) * IB <= io.xhi && v1 <= io.nvec && (v1 + 1) * OB <= io.yhi;
+    return v0 * IB >= rlo && (v1 + 1) * IB <= io.xhi && v1 <= io.nvec && (v1 + 1) * OB <= io.yhi;
 }
 
+// Loads of this wave's span in chunk c; rlo as for shift_interior
 template <int IB, int ESZ, int K, bool NT>
-__device__ __forceinline__ void shift_load(ShiftLoads<IB, K>& L, const ShiftIO& io, int64_t c) {
+__device__ __forceinline__ void shift_load(ShiftLoads<IB, K>& L, const ShiftIO& io, int64_t c, int64_t rlo) {
     const int lane = threadIdx.x & 63;
     const int64_t v0 = span_first<K>(c);
     L.e = dw_zero<IB / 4>();
     const int64_t v1 = v0 + K * 64;                    // the span's aligned input vectors [v0, v1]
-    if (v0 * IB >= io.mx && (v1 + 1) * IB <= io.xhi) {   // wave-uniform: all of them inside x, full loads
+    if (v0 * IB >= rlo && (v1 + 1) * IB <= io.xhi) {   // wave-uniform: all of them readable, full loads
         const char* base = io.xa + v0 * IB;   // wave-uniform; each lane adds a 32-bit offset
 #pragma unroll
         for (int k = 0; k < K; ++k) {
@@ -582,6 +598,10 @@ __device__ __forceinline__ void shift_load(ShiftLoads<IB, K>& L, const ShiftIO& 
 #pragma unroll
     for (int k = 0; k < K; ++k) L.a[k] = aligned_vec<IB, ESZ, NT>(io.xa, v0 + k * 64 + lane, io.mx, io.xhi);
     if (io.mx != 0 && lane == 63) L.e = aligned_vec<IB, ESZ, NT>(io.xa, v0 + K * 64, io.mx, io.xhi);
+}
+template <int IB, int ESZ, int K, bool NT>
+__device__ __forceinline__ void shift_load(ShiftLoads<IB, K>& L, const ShiftIO& io, int64_t c) {
+    shift_load<IB, ESZ, K, NT>(L, io, c, io.mx);
 }
 
 // Convert and store one loaded chunk: op(in, v, valid, k) maps lane vector
@@ -668,10 +688,16 @@ __device__ __forceinline__ void shift_convert_path(const ShiftLoads<IB, K>& L, c
     }
 }
 
+// rlo as for shift_interior (and as passed to the shift_load that filled L)
+template <int IB, int OB, int K, bool NT, int XDW, typename Op>
+__device__ __forceinline__ void shift_convert(const ShiftLoads<IB, K>& L, const ShiftIO& io, int64_t c, int64_t rlo,
+                                              Op&& op) {
+    if (shift_interior<IB, OB, K>(io, c, rlo)) shift_convert_path<IB, OB, K, NT, XDW, true>(L, io, c, op);   // per wave
+    else shift_convert_path<IB, OB, K, NT, XDW, false>(L, io, c, op);
+}
 template <int IB, int OB, int K, bool NT, int XDW, typename Op>
 __device__ __forceinline__ void shift_convert(const ShiftLoads<IB, K>& L, const ShiftIO& io, int64_t c, Op&& op) {
-    if (shift_interior<IB, OB, K>(io, c)) shift_convert_path<IB, OB, K, NT, XDW, true>(L, io, c, op);   // per wave
-    else shift_convert_path<IB, OB, K, NT, XDW, false>(L, io, c, op);
+    shift_convert<IB, OB, K, NT, XDW>(L, io, c, io.mx, op);
 }
 
 // ===========================================================================
@@ -1311,14 +1337,19 @@ k_channel_shift(const void* __restrict__ x, int64_t rows, int64_t cols, uint8_t*
     constexpr int ESZ = ESize<DT>::value;
     for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
         const ShiftIO io = shift_io<16, VE>((const char*)x + r * cols * ESZ, cols * ESZ, q + r * cols, cols, cols / VE);
+        // below the row's start lie the previous row's last bytes: readable,
+        // so the row's first wave can take full loads (not for the first row)
+        const int64_t rlo = r > 0 ? 0 : io.mx;
         ShiftLoads<16, K> L;
-        shift_load<16, ESZ, K, true>(L, io, 0);
+        shift_load<16, ESZ, K, true>(L, io, 0, rlo);
         HpVec<DT> h;
         h.r = v4u{L.e.d[0], L.e.d[1], L.e.d[2], L.e.d[3]};
         uint32_t m = h.absmax_bits();
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            h.r = v4u{L.a[k].d[0], L.a[k].d[1], L.a[k].d[2], L.a[k].d[3]};
+            Dw<4> a = L.a[k];
+            if (k == 0 && threadIdx.x == 0) a = zero_below(a, io.mx);   // drop the previous row's bytes
+            h.r = v4u{a.d[0], a.d[1], a.d[2], a.d[3]};
             m = umax(m, h.absmax_bits());
         }
         m = block_max256(m, lds);
@@ -1326,7 +1357,7 @@ k_channel_shift(const void* __restrict__ x, int64_t rows, int64_t cols, uint8_t*
         channel_scale<FMT>(m, scale, sinv);
         if (threadIdx.x == 0) sinv_out[r] = sinv;
         const bool saturate = needs_saturation(m, scale);   // uniform
-        shift_convert<16, VE, K, true, XDW>(L, io, 0, [&](const Dw<4>& in, int64_t, bool, int) {
+        shift_convert<16, VE, K, true, XDW>(L, io, 0, rlo, [&](const Dw<4>& in, int64_t, bool, int) {
             HpVec<DT> v;
             v.r = v4u{in.d[0], in.d[1], in.d[2], in.d[3]};
             float f[VE];
